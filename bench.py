@@ -1,0 +1,232 @@
+"""Benchmark of the biased multi-query attention hot path on one MI355X.
+
+One step = the full-context workload: 9 independent seeded layers (one per
+transformer block), each = pair-bias projection ([512,512,128] bf16 ->
+[8,512,512] fp32) + biased soft-capped MQA forward (B=1, S=8192, 8 query
+heads, 1 K/V head, d=128, bf16 inputs, fp32 accumulation), back to back on
+one stream with every input already resident in HBM.
+
+Prints ONE JSON line: attention TFLOP/s over the whole step (FLOPs =
+4*B*Hq*S^2*d per layer, non-causal QK^T + PV), the roofline of the dominant
+kernel (the attention) from HIP events on its own stream, and the CPU oracle
+timed on a bounded sample (one of the 9 layers) on this host's cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+#: MI355X published dense peaks used for the roofline.
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "biased_mqa_fwd_full_counters.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_flops(B, S, H=8, D=128):
+    return 4.0 * B * H * S * S * D
+
+
+def proj_bytes(P, C, H=8, elem=2):
+    return P * P * C * elem + C * H * elem + H * P * P * 4
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("biased_mqa_fwd.hip", "abg_internal.h"):
+        with open(os.path.join(ROOT, "long_context_biased_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(per_launch_flops_unit):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current kernel source; else None."""
+    try:
+        kv = {}
+        with open(COUNTERS_FILE) as f:
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_digest") != source_digest():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(layer):
+    """The oracle (unchanged) on one full layer: projection + all 8192 x 8
+    output rows, timed on this host's cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    bias = oracle.project_pair_bias(layer.pair, layer.weight)
+    oracle.attention(layer.q, layer.k, layer.v, bias, scale=layer.scale, cap=layer.cap)
+    dt = time.perf_counter() - t0
+    fl = attn_flops(layer.B, layer.S)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"1 of the 9 layers (projection + all {layer.S} positions x 8 heads), "
+                       f"float64 numpy, {dt:.1f} s wall; BLAS threads = cores")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=9)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    n_layers = args.layers
+
+    def to_gpu(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t0 = time.perf_counter()
+    layers, host0 = [], None
+    for li in range(n_layers):
+        L = workloads.make_layer("full", layer=li)
+        if li == 0:
+            host0 = L
+        t = {n: to_gpu(getattr(L, n)) for n in ("q", "k", "v", "pair", "weight")}
+        P = L.S // 16
+        t["bias"] = torch.empty((8, P, P), dtype=torch.float32, device=dev)
+        t["out"] = torch.empty_like(t["q"])
+        layers.append(t)
+    torch.cuda.synchronize()
+    log(f"inputs: {n_layers} layers generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    S = host0.S
+    P = S // 16
+    scale = host0.scale
+    cap = host0.cap
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        for li, t in enumerate(layers):
+            if events is not None:
+                events[li][0].record(stream)
+            pair_bias_project(t["pair"], t["weight"], out=t["bias"])
+            if events is not None:
+                events[li][1].record(stream)
+            biased_mqa_fwd(t["q"], t["k"], t["v"], t["bias"], out=t["out"], scale=scale,
+                           softcap=cap)
+            if events is not None:
+                events[li][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps between two events, no per-kernel events inside.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # Per-kernel durations: the same steps again, each launch bracketed by
+    # events on the launch stream.
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_layers)]
+          for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    proj_ms = [e[0].elapsed_time(e[1]) for st in ev for e in st]
+    attn_ms = [e[1].elapsed_time(e[2]) for st in ev for e in st]
+    attn_avg = float(np.mean(attn_ms))
+    proj_avg = float(np.mean(proj_ms))
+
+    fl_layer = attn_flops(1, S)
+    value = n_layers * fl_layer / (ms_per_step * 1e-3) / 1e12
+    achieved = fl_layer / (attn_avg * 1e-3) / 1e12
+    traffic = load_traffic(fl_layer)
+    pb = proj_bytes(P, 128)
+    log(f"step {ms_per_step:.3f} ms; attention avg {attn_avg * 1e3:.1f} us "
+        f"(median {np.median(attn_ms) * 1e3:.1f}, p95 {np.percentile(attn_ms, 95) * 1e3:.1f}) "
+        f"= {achieved:.1f} TFLOP/s; projection avg {proj_avg * 1e3:.1f} us = "
+        f"{pb / (proj_avg * 1e-3) / 1e9:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on one layer ...")
+        cpu = cpu_baseline(host0)
+        log(f"cpu baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": "biased-MQA fwd TFLOP/s at S=8192, H=8, d=128 bf16; % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(128) q,k,v; N(0,1) pair rep; W var 1/128)",
+        "config": {"workload": "full-context: 9 independent layers, each pair-bias projection "
+                               "+ biased soft-capped MQA fwd",
+                   "B": 1, "S": S, "P": P, "q_heads": 8, "kv_heads": 1, "d": 128,
+                   "pair_channels": 128, "layers": n_layers, "softcap": cap,
+                   "global_batch": 1, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "biased_mqa_fwd_kernel<bf16>",
+                     "avg_launch_us": round(attn_avg * 1e3, 2)},
+        "projection": {"bound": "hbm", "avg_launch_us": round(proj_avg * 1e3, 2),
+                       "bytes_per_launch": pb,
+                       "achieved_GBs": round(pb / (proj_avg * 1e-3) / 1e9, 1),
+                       "peak_GBs": PEAK_HBM_GBS,
+                       "frac": round(pb / (proj_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

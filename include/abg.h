@@ -1,0 +1,128 @@
+/*
+ * abg.h - C ABI of the biased multi-query attention library (libabg.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is AlphaGenome's sequence attention as described on the web
+ * page "Making Full-Context AlphaGenome Fit on an RTX 3090"
+ * (twigslot.github.io):
+ *
+ *   - section "Why stock FlashAttention was not a drop-in replacement":
+ *     Q [B,S,8,128], K [B,S,1,128], V [B,S,1,Dv] with one K/V head shared by
+ *     the 8 query heads; a compact learned bias with one cell per 16
+ *     positions on each axis; the logit equation
+ *         L_ij = cap * tanh((scale * q_i . k_j + bias[i/16, j/16]) / cap)
+ *     with cap 5 and scale 1/sqrt(128); softmax over keys; times V; BF16
+ *     matrix products with FP32 accumulation.
+ *   - section "Profiling pointed at one very large object": the compact bias
+ *     is a projection of a compact pair representation, repeated 16x along
+ *     both sequence axes in the dense implementation.
+ *   - section "Online softmax, one block at a time": the output is computed
+ *     tile by tile with running max / denominator / numerator, and the dense
+ *     logits and the dense repeated bias never exist.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors) owned by the caller.  Tensors are dense, row-major,
+ *     contiguous, 16-byte aligned.  The library never allocates, frees or
+ *     synchronizes; it only enqueues kernels on `stream` (a hipStream_t
+ *     passed as void*, NULL = the null stream) and returns.
+ *   - Every argument is validated on the host before any HIP call; a non-OK
+ *     status means nothing was enqueued.  abg_last_error() then gives a
+ *     thread-local message naming the argument.
+ *   - ABG_ERR_DEVICE means the HIP runtime rejected the launch; the message
+ *     carries the HIP error string.  Kernel faults surface, as usual for HIP,
+ *     at the caller's next synchronization.
+ *   - Calls are thread-safe; results are deterministic (no atomics).
+ */
+#ifndef ABG_H
+#define ABG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ABG_ABI_VERSION 1
+
+typedef enum abg_status {
+  ABG_OK = 0,
+  ABG_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  ABG_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent   */
+  ABG_ERR_UNSUPPORTED = 3, /* valid request that this build does not implement   */
+  ABG_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
+  ABG_ERR_VALUE = 5,       /* a scalar argument is not finite or out of range    */
+  ABG_ERR_ALIAS = 6,       /* the output overlaps an input                       */
+  ABG_ERR_DEVICE = 7       /* the HIP runtime reported an error                  */
+} abg_status;
+
+typedef enum abg_dtype {
+  ABG_F32 = 0,  /* IEEE float32 inputs, float32 products                   */
+  ABG_BF16 = 1  /* bfloat16 inputs, bf16 products with float32 accumulation */
+} abg_dtype;
+
+/* Version of this ABI (ABG_ABI_VERSION). */
+int abg_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* abg_status_string(int status);
+
+/* Thread-local detail for the last non-OK status returned on this thread
+ * ("" if none).  The pointer stays valid until the next library call on the
+ * same thread. */
+const char* abg_last_error(void);
+
+/*
+ * Pair-bias projection ("Profiling pointed at one very large object"):
+ *
+ *   bias[b, h, p, r] = sum_c pair[b, p, r, c] * weight[c, h]
+ *
+ * A plain linear map (no bias term, normalisation or activation).
+ *   pair    [Bp, P, P, C]  dtype      compact pair representation(s)
+ *   weight  [C, H]         dtype      projection weight, shared by all b
+ *   bias    [Bp, H, P, P]  float32    written fully (products in dtype,
+ *                                     accumulated in float32)
+ * Limits: Bp >= 1; 1 <= P <= 65536; 8 <= C <= 512 with C % 8 == 0; H == 8.
+ * bias must not overlap pair or weight.
+ */
+abg_status abg_pair_bias_project(const void* pair, const void* weight, float* bias,
+                                 int64_t Bp, int64_t P, int64_t C, int64_t H,
+                                 abg_dtype dtype, void* stream);
+
+/*
+ * Biased, soft-capped multi-query attention forward
+ * ("Why stock FlashAttention was not a drop-in replacement", logit equation;
+ *  "Online softmax, one block at a time"):
+ *
+ *   x_ij  = scale * (q[b,i,h,:] . k[b,j,0,:]) + bias_b[h, i/16, j/16]
+ *   L_ij  = softcap * tanh(x_ij / softcap)   (softcap > 0)
+ *         = x_ij                             (softcap == 0: no cap)
+ *   out[b,i,h,:] = sum_j softmax_j(L_i.) * v[b,j,0,:]
+ *
+ *   q     [B, S, Hq, Dk]  dtype
+ *   k     [B, S, 1, Dk]   dtype   (one K head shared by all query heads)
+ *   v     [B, S, 1, Dv]   dtype   (one V head shared by all query heads)
+ *   bias  float32 compact bias; batch item b reads the [Hq, S/16, S/16]
+ *         block at  bias + (b / bias_group) * bias_batch_stride  (elements).
+ *         bias_batch_stride = 0 shares one bias by every item; bias_group is
+ *         the number of consecutive items that share a block (e.g. 2 for a
+ *         REF/ALT pair).
+ *   out   [B, S, Hq, Dv]  dtype, written fully; must not overlap any input.
+ *
+ * Non-causal, no masks.  Limits (v1): B >= 1; S % 64 == 0 and
+ * 64 <= S <= 262144; Hq == 8; Dk == 128; Dv == 128; bias_group >= 1 and
+ * bias_batch_stride == 0 or >= Hq*(S/16)^2; scale finite; softcap finite and
+ * >= 0.
+ */
+abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
+                              const float* bias, void* out,
+                              int64_t B, int64_t S, int64_t Hq, int64_t Dk, int64_t Dv,
+                              int64_t bias_batch_stride, int64_t bias_group,
+                              float scale, float softcap,
+                              abg_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABG_H */

@@ -1,0 +1,187 @@
+"""ctypes binding of libabg.so (include/abg.h).
+
+Argument marshalling only: tensors are torch CUDA tensors (device memory),
+passed as raw pointers with the current stream; all arithmetic runs in the
+library's HIP kernels.  If the library has not been built the calls raise
+instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libabg.so")
+
+ABG_F32 = 0
+ABG_BF16 = 1
+
+STATUS = {0: "ABG_OK", 1: "ABG_ERR_NULL", 2: "ABG_ERR_SHAPE", 3: "ABG_ERR_UNSUPPORTED",
+          4: "ABG_ERR_ALIGN", 5: "ABG_ERR_VALUE", 6: "ABG_ERR_ALIAS", 7: "ABG_ERR_DEVICE"}
+
+#: Every symbol include/abg.h declares.
+EXPORTS = ("abg_abi_version", "abg_status_string", "abg_last_error",
+           "abg_pair_bias_project", "abg_biased_mqa_fwd")
+
+
+class AbgError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libabg.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    lib.abg_abi_version.restype = i32
+    lib.abg_abi_version.argtypes = []
+    lib.abg_status_string.restype = ctypes.c_char_p
+    lib.abg_status_string.argtypes = [i32]
+    lib.abg_last_error.restype = ctypes.c_char_p
+    lib.abg_last_error.argtypes = []
+    lib.abg_pair_bias_project.restype = i32
+    lib.abg_pair_bias_project.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.abg_biased_mqa_fwd.restype = i32
+    lib.abg_biased_mqa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                       i64, i64, f32, f32, i32, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().abg_last_error().decode(errors="replace")
+        raise AbgError(status, msg)
+
+
+# ---------------------------------------------------------------------------
+# Raw calls (pointers and sizes), as in include/abg.h
+# ---------------------------------------------------------------------------
+def raw_pair_bias_project(pair, weight, bias, Bp, P, C, H, dtype, stream=None) -> int:
+    return load().abg_pair_bias_project(pair, weight, bias, Bp, P, C, H, dtype, stream)
+
+
+def raw_biased_mqa_fwd(q, k, v, bias, out, B, S, Hq, Dk, Dv, bias_batch_stride,
+                       bias_group, scale, softcap, dtype, stream=None) -> int:
+    return load().abg_biased_mqa_fwd(q, k, v, bias, out, B, S, Hq, Dk, Dv,
+                                     bias_batch_stride, bias_group, scale, softcap,
+                                     dtype, stream)
+
+
+# ---------------------------------------------------------------------------
+# torch front end
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ABG_BF16
+    if t.dtype == torch.float32:
+        return ABG_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device) -> Optional[int]:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def pair_bias_project(pair, weight, out=None):
+    """bias[b, h, p, r] = sum_c pair[b, p, r, c] * weight[c, h].
+
+    ``pair`` [Bp, P, P, C] or [P, P, C] and ``weight`` [C, 8] of the same
+    dtype (bfloat16 or float32); returns float32 [Bp, 8, P, P] (or [8, P, P]).
+    """
+    import torch
+    _dev(pair, "pair")
+    _dev(weight, "weight")
+    squeeze = pair.dim() == 3
+    p4 = pair.unsqueeze(0) if squeeze else pair
+    if p4.dim() != 4 or p4.shape[1] != p4.shape[2]:
+        raise ValueError(f"pair must be [Bp, P, P, C], got {tuple(pair.shape)}")
+    Bp, P, _, C = p4.shape
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError(f"weight must be [C={C}, H], got {tuple(weight.shape)}")
+    if weight.dtype != pair.dtype:
+        raise TypeError("pair and weight must have the same dtype")
+    H = weight.shape[1]
+    if out is None:
+        out = torch.empty((Bp, H, P, P), dtype=torch.float32, device=pair.device)
+    _dev(out, "out")
+    if out.dtype != torch.float32 or out.numel() != Bp * H * P * P:
+        raise ValueError("out must be float32 [Bp, H, P, P]")
+    _check(raw_pair_bias_project(p4.data_ptr(), weight.data_ptr(), out.data_ptr(), Bp, P, C, H,
+                                 _dtype_code(pair), _stream(pair.device)))
+    return out[0] if (squeeze and out.dim() == 4) else out
+
+
+def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
+                   softcap: float = 5.0, bias_group: int = 1):
+    """Biased, soft-capped multi-query attention forward on the GPU.
+
+    ``q`` [B, S, 8, 128], ``k`` [B, S, 1, 128], ``v`` [B, S, 1, 128] (bfloat16
+    or float32); ``bias`` float32 compact bias [8, S/16, S/16] shared by all
+    items, or [Bb, 8, S/16, S/16] with item b reading block b // bias_group.
+    ``scale`` defaults to 1/sqrt(128); ``softcap`` 0 disables the cap.
+    Returns ``out`` [B, S, 8, 128] in the input dtype.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (bias, "bias")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, S, heads, D]")
+    B, S, Hq, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, S, 1, Dk) or tuple(v.shape[:3]) != (B, S, 1):
+        raise ValueError(f"k must be [B,S,1,Dk] and v [B,S,1,Dv]; got {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if bias.dtype != torch.float32:
+        raise TypeError("bias must be float32")
+    P = S // 16
+    if bias.dim() == 3:
+        bias_stride = 0
+        if tuple(bias.shape) != (Hq, P, P):
+            raise ValueError(f"bias must be [{Hq},{P},{P}], got {tuple(bias.shape)}")
+    elif bias.dim() == 4:
+        if tuple(bias.shape[1:]) != (Hq, P, P):
+            raise ValueError(f"bias must be [Bb,{Hq},{P},{P}], got {tuple(bias.shape)}")
+        bias_stride = 0 if bias.shape[0] == 1 else Hq * P * P
+        if bias.shape[0] > 1 and bias.shape[0] * bias_group < B:
+            raise ValueError("bias has too few items for B and bias_group")
+    else:
+        raise ValueError("bias must be 3-D or 4-D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    if out is None:
+        out = torch.empty((B, S, Hq, Dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out")
+    if out.dtype != q.dtype or tuple(out.shape) != (B, S, Hq, Dv):
+        raise ValueError("out must match q's dtype and be [B, S, Hq, Dv]")
+    _check(raw_biased_mqa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(),
+                              out.data_ptr(), B, S, Hq, Dk, Dv, bias_stride, bias_group,
+                              float(scale), float(softcap), _dtype_code(q), _stream(q.device)))
+    return out

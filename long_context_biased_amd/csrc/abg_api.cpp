@@ -1,0 +1,149 @@
+// C ABI of libabg: argument validation and dispatch to the HIP launchers.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// enqueues nothing and touches no device state (and can be exercised on a
+// machine without a GPU).  Contract: include/abg.h.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "abg_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+abg_status fail(abg_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+abg_status fail(abg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+int64_t elem_bytes(abg_dtype d) { return d == ABG_BF16 ? 2 : 4; }
+
+abg_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ABG_OK;
+  return fail(ABG_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int abg_abi_version(void) { return ABG_ABI_VERSION; }
+
+const char* abg_status_string(int status) {
+  switch (status) {
+    case ABG_OK: return "ABG_OK";
+    case ABG_ERR_NULL: return "ABG_ERR_NULL";
+    case ABG_ERR_SHAPE: return "ABG_ERR_SHAPE";
+    case ABG_ERR_UNSUPPORTED: return "ABG_ERR_UNSUPPORTED";
+    case ABG_ERR_ALIGN: return "ABG_ERR_ALIGN";
+    case ABG_ERR_VALUE: return "ABG_ERR_VALUE";
+    case ABG_ERR_ALIAS: return "ABG_ERR_ALIAS";
+    case ABG_ERR_DEVICE: return "ABG_ERR_DEVICE";
+    default: return "ABG_UNKNOWN_STATUS";
+  }
+}
+
+const char* abg_last_error(void) { return g_last_error.c_str(); }
+
+abg_status abg_pair_bias_project(const void* pair, const void* weight, float* bias,
+                                 int64_t Bp, int64_t P, int64_t C, int64_t H,
+                                 abg_dtype dtype, void* stream) {
+  g_last_error.clear();
+  if (dtype != ABG_F32 && dtype != ABG_BF16)
+    return fail(ABG_ERR_VALUE, "dtype %d is not ABG_F32 or ABG_BF16", (int)dtype);
+  if (!pair) return fail(ABG_ERR_NULL, "pair is NULL");
+  if (!weight) return fail(ABG_ERR_NULL, "weight is NULL");
+  if (!bias) return fail(ABG_ERR_NULL, "bias is NULL");
+  if (Bp < 1) return fail(ABG_ERR_SHAPE, "Bp = %lld must be >= 1", (long long)Bp);
+  if (P < 1 || P > 65536) return fail(ABG_ERR_SHAPE, "P = %lld must be in [1, 65536]", (long long)P);
+  if (C < 8 || C > 512 || C % 8 != 0)
+    return fail(ABG_ERR_UNSUPPORTED, "C = %lld must be a multiple of 8 in [8, 512]", (long long)C);
+  if (H != 8) return fail(ABG_ERR_UNSUPPORTED, "H = %lld: only 8 heads are supported", (long long)H);
+  if (Bp > (int64_t(1) << 40) / (P * P))
+    return fail(ABG_ERR_SHAPE, "Bp * P * P is too large");
+  if (!aligned16(pair)) return fail(ABG_ERR_ALIGN, "pair is not 16-byte aligned");
+  if (!aligned16(weight)) return fail(ABG_ERR_ALIGN, "weight is not 16-byte aligned");
+  if (!aligned16(bias)) return fail(ABG_ERR_ALIGN, "bias is not 16-byte aligned");
+  const int64_t E = elem_bytes(dtype);
+  const int64_t out_bytes = Bp * H * P * P * 4;
+  if (overlaps(bias, out_bytes, pair, Bp * P * P * C * E))
+    return fail(ABG_ERR_ALIAS, "bias overlaps pair");
+  if (overlaps(bias, out_bytes, weight, C * H * E))
+    return fail(ABG_ERR_ALIAS, "bias overlaps weight");
+  hipError_t e = abg::launch_pair_bias_project(pair, weight, bias, Bp, P, C, dtype,
+                                               static_cast<hipStream_t>(stream));
+  return device_status(e, "pair_bias_project launch");
+}
+
+abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
+                              const float* bias, void* out,
+                              int64_t B, int64_t S, int64_t Hq, int64_t Dk, int64_t Dv,
+                              int64_t bias_batch_stride, int64_t bias_group,
+                              float scale, float softcap,
+                              abg_dtype dtype, void* stream) {
+  g_last_error.clear();
+  if (dtype != ABG_F32 && dtype != ABG_BF16)
+    return fail(ABG_ERR_VALUE, "dtype %d is not ABG_F32 or ABG_BF16", (int)dtype);
+  if (!q) return fail(ABG_ERR_NULL, "q is NULL");
+  if (!k) return fail(ABG_ERR_NULL, "k is NULL");
+  if (!v) return fail(ABG_ERR_NULL, "v is NULL");
+  if (!bias) return fail(ABG_ERR_NULL, "bias is NULL");
+  if (!out) return fail(ABG_ERR_NULL, "out is NULL");
+  if (B < 1 || B > 65535) return fail(ABG_ERR_SHAPE, "B = %lld must be in [1, 65535]", (long long)B);
+  if (S < 64 || S > 262144)
+    return fail(ABG_ERR_SHAPE, "S = %lld must be in [64, 262144]", (long long)S);
+  if (S % 64 != 0)
+    return fail(ABG_ERR_UNSUPPORTED, "S = %lld: only whole 64-position tiles are supported", (long long)S);
+  if (Hq != 8) return fail(ABG_ERR_UNSUPPORTED, "Hq = %lld: only 8 query heads are supported", (long long)Hq);
+  if (Dk != 128) return fail(ABG_ERR_UNSUPPORTED, "Dk = %lld: only 128 is supported", (long long)Dk);
+  if (Dv != 128) return fail(ABG_ERR_UNSUPPORTED, "Dv = %lld: only 128 is supported", (long long)Dv);
+  if (!std::isfinite(scale)) return fail(ABG_ERR_VALUE, "scale is not finite");
+  if (!std::isfinite(softcap) || softcap < 0.f)
+    return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
+  if (bias_group < 1 || bias_group > B)
+    return fail(ABG_ERR_SHAPE, "bias_group = %lld must be in [1, B]", (long long)bias_group);
+  const int64_t P = S / 16;
+  const int64_t bias_elems = Hq * P * P;
+  if (bias_batch_stride != 0 && bias_batch_stride < bias_elems)
+    return fail(ABG_ERR_SHAPE, "bias_batch_stride = %lld must be 0 or >= Hq*(S/16)^2 = %lld",
+                (long long)bias_batch_stride, (long long)bias_elems);
+  if (bias_batch_stride % 4 != 0)
+    return fail(ABG_ERR_ALIGN, "bias_batch_stride must be a multiple of 4 elements");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(out))
+    return fail(ABG_ERR_ALIGN, "q, k, v, bias and out must be 16-byte aligned");
+  const int64_t E = elem_bytes(dtype);
+  const int64_t q_bytes = B * S * Hq * Dk * E;
+  const int64_t kv_bytes = B * S * Dk * E;
+  const int64_t n_bias = (B - 1) / bias_group + 1;
+  const int64_t bias_bytes = ((n_bias - 1) * bias_batch_stride + bias_elems) * 4;
+  const int64_t out_bytes = B * S * Hq * Dv * E;
+  if (overlaps(out, out_bytes, q, q_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps q");
+  if (overlaps(out, out_bytes, k, kv_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps k");
+  if (overlaps(out, out_bytes, v, B * S * Dv * E)) return fail(ABG_ERR_ALIAS, "out overlaps v");
+  if (overlaps(out, out_bytes, bias, bias_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps bias");
+
+  abg::AttnLaunch a{q, k, v, bias, out, B, S, bias_batch_stride, bias_group,
+                    scale, softcap, dtype};
+  hipError_t e = abg::launch_biased_mqa_fwd(a, static_cast<hipStream_t>(stream));
+  return device_status(e, "biased_mqa_fwd launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+"""Element-by-element comparison of a GPU result with the float64 oracle.
+
+Tolerances:
+* max-abs 1e-4 (float32 inputs) and 2e-2 (bf16 inputs) on the attention
+  output: the contract values.
+* relative L2 error ||got - ref|| / ||ref||: 1e-5 (float32) and 1e-2 (bf16).
+  Derivation: the float32 path rounds products and sums to float32 and
+  evaluates exp2/rcp to about 1 ulp, so a few 1e-7 relative per logit and a
+  few 1e-6 relative on p = exp(L - cap) (the exponent reaches 14.4 in base 2)
+  -> ~1e-6 on the output, 10x margin.  The bf16 path rounds every probability
+  and every output to bf16 (half an ulp = 2^-8 relative at most, about 2^-9.5
+  RMS), so ~2e-3 relative L2, 5x margin.
+  Without this second bound the checker could not reject several wrong
+  kernels at the workloads' own input distribution, where |out| is ~1e-2
+  (tests/test_checker_strength.py shows which).
+* the pair-bias projection (float32 accumulation of exact products of C
+  terms): relative L2 1e-6 and max-abs 1e-5 * max|ref|, both with margin
+  over C * 2^-24 accumulation error.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ATTN_TOL = {"f32": dict(max_abs=1e-4, rel_l2=1e-5),
+            "bf16": dict(max_abs=2e-2, rel_l2=1e-2)}
+PROJ_TOL = dict(rel_l2=1e-6, max_abs_rel=1e-5)
+
+
+def stats(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    denom = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff)) / denom if denom > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def attention_ok(got, ref, dtype):
+    """(ok, max_abs, rel_l2) against the attention tolerances of ``dtype``."""
+    tol = ATTN_TOL[dtype]
+    if not np.all(np.isfinite(got)):
+        return False, float("inf"), float("inf")
+    max_abs, rel = stats(got, ref)
+    return (max_abs <= tol["max_abs"] and rel <= tol["rel_l2"]), max_abs, rel
+
+
+def projection_ok(got, ref):
+    if not np.all(np.isfinite(got)):
+        return False, float("inf"), float("inf")
+    max_abs, rel = stats(got, ref)
+    scale = max(1e-30, float(np.max(np.abs(ref))))
+    return (rel <= PROJ_TOL["rel_l2"] and max_abs <= PROJ_TOL["max_abs_rel"] * scale), max_abs, rel

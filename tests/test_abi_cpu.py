@@ -1,0 +1,141 @@
+"""The C ABI on the host: the library loads, exports every symbol that
+include/abg.h declares, and rejects every invalid argument with its status
+code before any HIP call (so these run without a GPU; no kernel is launched).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_biased_amd as abg
+from long_context_biased_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "abg.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, VALUE, ALIAS, DEVICE = range(8)
+
+# Fake, distinct, 16-byte aligned "device" addresses: validation never
+# dereferences them, and every call below fails validation.
+Q, K, V, BIAS, OUT = (0x100000000 * (i + 1) for i in range(5))
+BF16, F32 = abg.ABG_BF16, abg.ABG_F32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:abg_status|int|const char\*)\s+(abg_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = abg.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    lib = abg.load()
+    assert lib.abg_abi_version() == 1
+    for code, name in _lib.STATUS.items():
+        assert lib.abg_status_string(code).decode() == name
+    assert lib.abg_status_string(99).decode() == "ABG_UNKNOWN_STATUS"
+
+
+def attn(**kw):
+    a = dict(q=Q, k=K, v=V, bias=BIAS, out=OUT, B=1, S=8192, Hq=8, Dk=128, Dv=128,
+             bias_batch_stride=0, bias_group=1, scale=0.088, softcap=5.0, dtype=BF16)
+    a.update(kw)
+    return abg.raw_biased_mqa_fwd(a["q"], a["k"], a["v"], a["bias"], a["out"], a["B"], a["S"],
+                                  a["Hq"], a["Dk"], a["Dv"], a["bias_batch_stride"],
+                                  a["bias_group"], a["scale"], a["softcap"], a["dtype"], None)
+
+
+ATTN_CASES = [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL),
+    (dict(bias=None), NULL), (dict(out=None), NULL),
+    (dict(B=0), SHAPE), (dict(B=70000), SHAPE),
+    (dict(S=0), SHAPE), (dict(S=32), SHAPE), (dict(S=262144 + 64), SHAPE),
+    (dict(S=8192 + 16), UNSUP), (dict(S=100), UNSUP),
+    (dict(Hq=4), UNSUP), (dict(Hq=16), UNSUP),
+    (dict(Dk=64), UNSUP), (dict(Dv=192), UNSUP),
+    (dict(scale=float("nan")), VALUE), (dict(scale=float("inf")), VALUE),
+    (dict(softcap=-1.0), VALUE), (dict(softcap=float("inf")), VALUE),
+    (dict(softcap=float("nan")), VALUE),
+    (dict(dtype=7), VALUE),
+    (dict(bias_group=0), SHAPE), (dict(B=2, bias_group=3), SHAPE),
+    (dict(B=2, bias_batch_stride=100), SHAPE),
+    (dict(B=2, bias_batch_stride=8 * 512 * 512 + 2), ALIGN),
+    (dict(q=Q + 8), ALIGN), (dict(k=K + 4), ALIGN), (dict(v=V + 2), ALIGN),
+    (dict(bias=BIAS + 12), ALIGN), (dict(out=OUT + 8), ALIGN),
+    (dict(out=Q), ALIAS), (dict(out=Q + 16 * 1024 * 1024 - 16), ALIAS),
+    (dict(out=K), ALIAS), (dict(out=V), ALIAS), (dict(out=BIAS), ALIAS),
+    (dict(out=K - 16 * 1024 * 1024 + 16), ALIAS),
+]
+
+
+@pytest.mark.parametrize("kw,code", ATTN_CASES, ids=lambda x: str(x))
+def test_attention_rejects(kw, code):
+    st = attn(**kw)
+    assert st == code, (st, abg.load().abg_last_error())
+    assert abg.load().abg_last_error().decode()
+
+
+def proj(**kw):
+    a = dict(pair=Q, weight=K, bias=BIAS, Bp=1, P=512, C=128, H=8, dtype=BF16)
+    a.update(kw)
+    return abg.raw_pair_bias_project(a["pair"], a["weight"], a["bias"], a["Bp"], a["P"],
+                                     a["C"], a["H"], a["dtype"], None)
+
+
+PROJ_CASES = [
+    (dict(pair=None), NULL), (dict(weight=None), NULL), (dict(bias=None), NULL),
+    (dict(Bp=0), SHAPE), (dict(P=0), SHAPE), (dict(P=70000), SHAPE),
+    (dict(C=0), UNSUP), (dict(C=12), UNSUP), (dict(C=1024), UNSUP),
+    (dict(H=4), UNSUP), (dict(dtype=3), VALUE),
+    (dict(pair=Q + 8), ALIGN), (dict(weight=K + 2), ALIGN), (dict(bias=BIAS + 4), ALIGN),
+    (dict(bias=Q + 1024), ALIAS), (dict(bias=K), ALIAS),
+]
+
+
+@pytest.mark.parametrize("kw,code", PROJ_CASES, ids=lambda x: str(x))
+def test_projection_rejects(kw, code):
+    st = proj(**kw)
+    assert st == code, (st, abg.load().abg_last_error())
+
+
+def test_error_message_is_thread_local_and_cleared():
+    import threading
+    lib = abg.load()
+    assert attn(q=None) == NULL
+    msg = lib.abg_last_error().decode()
+    assert "q" in msg
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.abg_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert attn(Dk=64) == UNSUP
+    assert "Dk" in lib.abg_last_error().decode()
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64, 8, 128)
+    with pytest.raises(ValueError):
+        abg.biased_mqa_fwd(q, q[:, :, :1], q[:, :, :1], torch.zeros(8, 4, 4))
+    with pytest.raises(ValueError):
+        abg.pair_bias_project(torch.zeros(4, 4, 8), torch.zeros(8, 8))
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load(str(tmp_path / "nope.so"))

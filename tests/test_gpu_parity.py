@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Every case uses seeded inputs from ``long_context_biased_amd.workloads``; the
+oracle computes its own bias from the same pair representation and weight
+(never from a GPU result).  Small and medium shapes are compared on every
+output; full-size workloads on sampled query positions (all heads, all batch
+items), in the launch configuration the benchmark times.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import sample_rows, to_gpu, to_host, upload
+from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, workloads
+from parity import attention_ok, projection_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_layer(layer, dev):
+    """GPU hot path of one layer: projection then attention."""
+    t = upload(layer, dev)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    out = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, scale=layer.scale,
+                         softcap=layer.cap, bias_group=layer.bias_group)
+    torch.cuda.synchronize()
+    return to_host(bias), to_host(out)
+
+
+def _oracle_bias(layer):
+    return oracle.project_pair_bias(layer.pair, layer.weight)
+
+
+def _check_rows(layer, out, bias64, rows, batches=None):
+    batches = range(layer.B) if batches is None else batches
+    worst = (0.0, 0.0)
+    for b in batches:
+        ref = oracle.attention_rows(layer.q, layer.k, layer.v, bias64, rows, scale=layer.scale,
+                                    cap=layer.cap, bias_index=layer.bias_index, batch=b)
+        ok, ma, rel = attention_ok(out[b, rows], ref, layer.dtype)
+        assert ok, f"{layer.name} item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+        worst = (max(worst[0], ma), max(worst[1], rel))
+    print(f"  {layer.name} S={layer.S} B={layer.B} {layer.dtype}: worst max-abs {worst[0]:.3g} "
+          f"rel-L2 {worst[1]:.3g}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Projection
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "mid", "full", "variant", "stress", "stress_f32"])
+def test_projection_parity(name):
+    layer = workloads.make_layer(name)
+    t = upload(layer)
+    got = to_host(pair_bias_project(t["pair"], t["weight"]))
+    ref = _oracle_bias(layer)
+    ok, ma, rel = projection_ok(got, ref)
+    assert ok, f"{name}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+def test_projection_small_shapes():
+    for seed, (Bp, P, C, dt) in enumerate([(1, 1, 8, "f32"), (3, 5, 24, "bf16"),
+                                          (2, 33, 136, "f32"), (1, 64, 512, "bf16"),
+                                          (1, 7, 200, "bf16")]):
+        L = workloads.make_custom(B=Bp, S=max(16, 16 * P), dtype=dt, C=C, seed=seed)
+        pair = L.pair[:, :P, :P, :]
+        got = to_host(pair_bias_project(to_gpu(pair), to_gpu(L.weight)))
+        ok, ma, rel = projection_ok(got, oracle.project_pair_bias(pair, L.weight))
+        assert ok, f"case {seed}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+# ---------------------------------------------------------------------------
+# Attention: every output at small and medium sizes
+# ---------------------------------------------------------------------------
+SMALL = [
+    # B, S, dtype, cap, qkv_std, bias_std, n_pairs
+    (1, 64, "f32", 5.0, 1.0, 2.0, None),
+    (1, 64, "bf16", 5.0, 1.0, 2.0, None),
+    (2, 128, "bf16", 5.0, 0.09, 1.0, None),
+    (3, 192, "f32", 5.0, 1.0, 2.0, 1),
+    (2, 320, "bf16", 0.0, 1.0, 2.0, None),
+    (2, 320, "f32", 0.0, 1.0, 2.0, None),
+    (4, 256, "bf16", 1.5, 1.0, 3.0, 2),
+    (1, 1024, "f32", 5.0, 1.5, 2.0, None),
+    (1, 1024, "bf16", 0.0, 0.5, 1.0, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%d_S%d_%s_cap%g_%s" % (c[0], c[1], c[2], c[3], c[6]))
+def test_attention_small(case):
+    B, S, dt, cap, qstd, bstd, n_pairs = case
+    L = workloads.make_custom(B=B, S=S, dtype=dt, C=16, seed=S + B, qkv_std=qstd,
+                              bias_std=bstd, n_pairs=n_pairs)
+    L.cap = cap
+    bias_gpu, out = _run_layer(L, "cuda")
+    bias64 = _oracle_bias(L)
+    ref = oracle.attention(L.q, L.k, L.v, bias64, scale=L.scale, cap=cap, bias_index=L.bias_index)
+    ok, ma, rel = attention_ok(out, ref, dt)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+@pytest.mark.parametrize("hot", [False, True], ids=["base", "hot"])
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_attention_tiny_mid(name, hot):
+    L = workloads.make_layer(name, hot=hot)
+    bias_gpu, out = _run_layer(L, "cuda")
+    bias64 = _oracle_bias(L)
+    ok, ma, rel = projection_ok(bias_gpu, bias64)
+    assert ok, f"projection: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+    ref = oracle.attention(L.q, L.k, L.v, bias64, scale=L.scale, cap=L.cap)
+    ok, ma, rel = attention_ok(out, ref, L.dtype)
+    print(f"  {name}{' hot' if hot else ''}: max-abs {ma:.3g} rel-L2 {rel:.3g}", flush=True)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+# ---------------------------------------------------------------------------
+# Attention: full-size workloads on sampled query positions
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("layer_idx,hot", [(0, False), (8, False), (0, True)],
+                         ids=["layer0", "layer8", "layer0_hot"])
+def test_attention_full_sampled(layer_idx, hot):
+    L = workloads.make_layer("full", layer=layer_idx, hot=hot)
+    _, out = _run_layer(L, "cuda")
+    _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=layer_idx))
+
+
+@pytest.mark.parametrize("hot", [False, True], ids=["base", "hot"])
+def test_attention_variant_sampled(hot):
+    L = workloads.make_layer("variant", hot=hot)
+    _, out = _run_layer(L, "cuda")
+    _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=7))
+
+
+@pytest.mark.parametrize("name", ["stress", "stress_f32"])
+def test_attention_stress_sampled(name):
+    L = workloads.make_layer(name)
+    _, out = _run_layer(L, "cuda")
+    _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=3, extra=8))
+
+
+# ---------------------------------------------------------------------------
+# Properties that hold at any size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_equal_values_and_zero_logits(dt):
+    """All V rows equal -> out = that row; q = 0 and bias = 0 -> out = mean(V)."""
+    S = 8192
+    L = workloads.make_custom(B=1, S=S, dtype=dt, C=16, seed=11)
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    v_row = t["v"][:, :1].expand(-1, S, -1, -1).contiguous()
+    out = to_host(biased_mqa_fwd(t["q"], t["k"], v_row, bias))
+    u = to_host(v_row[0, 0, 0])
+    # Exact in real arithmetic.  The numerator and denominator are fp32 sums
+    # of S terms (about sqrt(S) * 2^-24 relative each, 3e-5 is 5 sigma at
+    # S = 8192); bf16 adds one output rounding (2^-8 relative).
+    rtol = 2.0 ** -8 + 3e-5 if dt == "bf16" else 3e-5
+    assert np.all(np.abs(out - u) <= rtol * np.abs(u) + 1e-6)
+    zq = torch.zeros_like(t["q"])
+    zb = torch.zeros_like(bias)
+    out = to_host(biased_mqa_fwd(zq, t["k"], t["v"], zb))
+    mean = oracle.as_f64(L.v)[0, :, 0, :].mean(0)
+    atol = 1e-5
+    assert np.all(np.abs(out - mean) <= rtol * np.abs(mean) + atol)
+
+
+def test_deterministic_and_stream_ordered():
+    """Bitwise-identical results across launches and on a side stream."""
+    L = workloads.make_layer("full", layer=1)
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    ref = biased_mqa_fwd(t["q"], t["k"], t["v"], bias)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        bias2 = pair_bias_project(t["pair"], t["weight"])
+        outs = [biased_mqa_fwd(t["q"], t["k"], t["v"], bias2) for _ in range(3)]
+    s.synchronize()
+    assert torch.equal(bias, bias2)
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
+def test_library_allocates_nothing():
+    """Only the caller's tensors exist: the library allocates no device memory
+    (no dense logits, no dense bias)."""
+    L = workloads.make_layer("full", layer=2)
+    t = upload(L)
+    bias = torch.empty((8, L.S // 16, L.S // 16), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(t["q"])
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    free_before, _ = torch.cuda.mem_get_info()
+    pair_bias_project(t["pair"], t["weight"], out=bias)
+    biased_mqa_fwd(t["q"], t["k"], t["v"], bias, out=out)
+    torch.cuda.synchronize()
+    free_after, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.max_memory_allocated() == before
+    # no allocation outside torch either (tolerate 64 MiB of runtime slack,
+    # far below the 2 GiB dense logit tensor or the 512 MiB dense bias)
+    assert free_before - free_after < 64 * 2 ** 20
+
+
+def test_bias_group_and_stride():
+    """bias_group = 2 with a [2, 8, P, P] bias equals passing each item its own
+    copy; a shared [8, P, P] bias equals stride 0."""
+    L = workloads.make_custom(B=4, S=256, dtype="bf16", C=16, seed=5, n_pairs=2)
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])          # [2, 8, P, P]
+    a = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, bias_group=2)
+    full = bias.repeat_interleave(2, dim=0).contiguous()      # [4, 8, P, P]
+    b = biased_mqa_fwd(t["q"], t["k"], t["v"], full)
+    assert torch.equal(a, b)
+    c = biased_mqa_fwd(t["q"], t["k"], t["v"], bias[0].contiguous())
+    d = biased_mqa_fwd(t["q"], t["k"], t["v"], bias[:1].expand(4, -1, -1, -1).contiguous())
+    assert torch.equal(c, d)

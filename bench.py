@@ -216,7 +216,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "biased_mqa_fwd_kernel<bf16>",
+                     "kernel": "biased_mqa_fwd_bf16_capped_kernel",
                      "avg_launch_us": round(attn_avg * 1e3, 2)},
         "projection": {"bound": "hbm", "avg_launch_us": round(proj_avg * 1e3, 2),
                        "bytes_per_launch": pb,

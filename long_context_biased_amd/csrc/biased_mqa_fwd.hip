@@ -22,18 +22,26 @@
 //     (r, g) then holds 16 scores of its own query row, so row sums need no
 //     cross-lane traffic until the end, and the probabilities feed the PV
 //     MFMA (O^T = V^T . P^T) as its B operand straight from registers.  The
-//     keys loaded into A are permuted (bits 2 and 3 of the row swapped) so
-//     that each lane's 8-value B fragment covers 8 consecutive keys;
+//     keys loaded into A are permuted (bits 2 and 3 of the row swapped; the
+//     permutation is applied when K is staged in LDS) so that each lane's
+//     8-value B fragment covers 8 consecutive keys;
 //   * V is transposed into LDS (V^T, keys contiguous) while it is staged, so
 //     a PV A operand is one 16-byte LDS read per lane;
+//   * LDS rows are padded by 16 bytes (K: 272 B, V^T: 144 B for bf16) so the
+//     32 rows read by a half-wave fall in distinct banks and every fragment
+//     address is one per-lane base plus an immediate offset;
 //   * the compact bias cells of a tile (8 heads x 2 position cells x 4 key
 //     cells) are staged with the tile, pre-multiplied by the exponent-domain
 //     constant; the index (i>>4, j>>4) is fixed per lane and register;
 //   * software pipeline: a 64-key tile is two 32-key halves.  Each stage
-//     issues 16 MFMAs (PV of one half + QK^T of the next tile's half) and, in
-//     between, the soft-cap/softmax VALU chain of another half, so the matrix
-//     cores and the VALU work at the same time inside one wave; the second
-//     wave on the SIMD fills the remaining gaps;
+//     issues 16 MFMAs (PV of one half + QK^T of the next tile's half) and,
+//     woven between them, the soft-cap/softmax chain of another half, so the
+//     matrix cores and the VALU work at the same time inside one wave; the
+//     second wave on the SIMD fills the remaining gaps.  For bf16 with the
+//     cap the order is fixed by hand: 16 slots of {LDS read three MFMAs
+//     ahead, one MFMA, six softmax micro-ops}, the softmax written as a
+//     skewed pipeline over its 16 values so dependent operations are far
+//     apart;
 //   * LDS tiles are triple-buffered for bf16 (one barrier per tile) and
 //     double-buffered for float32 (two barriers per tile, LDS budget); the
 //     global loads of tile t+3 are in flight while tile t computes.
@@ -62,8 +70,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -73,6 +81,11 @@ constexpr int kTileKeys = 64;  // keys per LDS tile
 constexpr int kBlockPos = 32;  // query positions per workgroup
 constexpr int kThreads = 64 * kHeads;
 constexpr float kLog2e = 1.4426950408889634f;
+// Heads per wave of the bf16 soft-capped kernel (2: four waves, one per SIMD).
+#ifndef ABG_FAST_HPW
+#define ABG_FAST_HPW 1
+#endif
+constexpr int kFastHeadsPerWave = ABG_FAST_HPW;
 
 template <typename T> struct Traits;
 template <> struct Traits<__bf16> {
@@ -89,19 +102,21 @@ template <> struct Traits<float> {
 template <typename T>
 struct Lay {
   static constexpr int E = sizeof(T);
-  static constexpr int K_ROW = kD * E;           // bytes per K row in LDS
-  static constexpr int K_CHUNKS = K_ROW / 16;    // 16-B chunks per K row
-  static constexpr int VT_ROW = kTileKeys * E;   // bytes per V^T row in LDS
-  static constexpr int VT_CHUNKS = VT_ROW / 16;
-  static constexpr int K_BYTES = kTileKeys * K_ROW;
-  static constexpr int VT_BYTES = kD * VT_ROW;
+  static constexpr int K_ROW = kD * E;            // payload bytes per K row
+  static constexpr int K_STRIDE = K_ROW + 16;     // padded row pitch in LDS
+  static constexpr int K_CHUNKS = K_ROW / 16;     // 16-B chunks per K row
+  static constexpr int VT_ROW = kTileKeys * E;    // payload bytes per V^T row
+  static constexpr int VT_STRIDE = VT_ROW + 16;
+  static constexpr int K_BYTES = kTileKeys * K_STRIDE;
+  static constexpr int VT_BYTES = kD * VT_STRIDE;
   static constexpr int BIAS_OFF = K_BYTES + VT_BYTES;
-  static constexpr int STAGE = BIAS_OFF + 256;   // + 64 bias floats
+  static constexpr int STAGE = BIAS_OFF + 256;    // + 64 bias floats
   static constexpr int NBUF = Traits<T>::NBUF;
-  static constexpr int OUT_ROW = kHeads * kD * E;  // output bytes per position
+  static constexpr int OUT_ROW = kHeads * kD * E; // output bytes per position
   static constexpr int OUT_BYTES = kBlockPos * OUT_ROW;
   static constexpr int SMEM = (NBUF * STAGE > OUT_BYTES) ? NBUF * STAGE : OUT_BYTES;
   static constexpr int K_PT = (kTileKeys * K_CHUNKS) / kThreads;  // K chunks per thread
+  static constexpr int K_ROWS_PER_PASS = kThreads / K_CHUNKS;
   static_assert(K_PT * kThreads == kTileKeys * K_CHUNKS, "K tile split");
   static_assert(kThreads == 512, "one 4x4 V block per thread");
 };
@@ -114,17 +129,15 @@ __device__ __forceinline__ void mfma(f32x16& acc, const f32x8& a, const f32x8& b
   for (int m = 0; m < 8; ++m) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], b[m], acc, 0, 0, 0);
 }
 
-// A fragment of 8 consecutive elements at byte offset `off` of LDS; float32
-// fragments are two 16-byte chunks (c, c ^ 1 after the swizzle).
+// 8 consecutive elements at byte offset `off` of LDS.
 template <typename T>
-__device__ __forceinline__ typename Traits<T>::F lds_frag(const char* base, int off0, int off1) {
+__device__ __forceinline__ typename Traits<T>::F lds_frag(const char* base, int off) {
   using F = typename Traits<T>::F;
   if constexpr (sizeof(T) == 2) {
-    (void)off1;
-    return *reinterpret_cast<const F*>(base + off0);
+    return *reinterpret_cast<const F*>(base + off);
   } else {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + off0);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + off1);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + off);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + off + 16);
     F f;
     __builtin_memcpy(&f, &lo, 16);
     __builtin_memcpy(reinterpret_cast<char*>(&f) + 16, &hi, 16);
@@ -144,16 +157,15 @@ struct Staged {
 };
 
 // Per-thread addresses of the staging copy (loop invariant).
-template <typename T>
 struct StageAddr {
-  int k_lds[Lay<T>::K_PT];
-  int v_glb;       // bytes from the tile base to this thread's first V row
-  int v_lds[4];    // V^T destinations of the 4 columns of the 4x4 block
+  int k_lds;       // LDS byte offset of this thread's first K chunk
+  int v_glb;       // bytes from the V tile base to this thread's first V row
+  int v_lds;       // LDS byte offset of the first V^T row of this thread's block
   int64_t b_glb;   // element offset of this thread's bias cell (tile 0)
 };
 
 template <typename T>
-__device__ __forceinline__ void load_tile(Staged<T>& st, const StageAddr<T>& ad, const char* kb,
+__device__ __forceinline__ void load_tile(Staged<T>& st, const StageAddr& ad, const char* kb,
                                           const char* vb, const float* bias_b, int t, int tid,
                                           float beta_mul) {
   using L = Lay<T>;
@@ -165,15 +177,16 @@ __device__ __forceinline__ void load_tile(Staged<T>& st, const StageAddr<T>& ad,
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     st.v[e] = *reinterpret_cast<const typename Traits<T>::VRow*>(vt + e * kD * L::E);
-  if (tid < 64) st.bias = bias_b[ad.b_glb + t * 4] * beta_mul;
+  st.bias = bias_b[ad.b_glb + t * 4] * beta_mul;
 }
 
 template <typename T>
-__device__ __forceinline__ void store_tile(const Staged<T>& st, const StageAddr<T>& ad, char* buf,
+__device__ __forceinline__ void store_tile(const Staged<T>& st, const StageAddr& ad, char* buf,
                                            int tid) {
   using L = Lay<T>;
 #pragma unroll
-  for (int i = 0; i < L::K_PT; ++i) *reinterpret_cast<u32x4*>(buf + ad.k_lds[i]) = st.k[i];
+  for (int i = 0; i < L::K_PT; ++i)
+    *reinterpret_cast<u32x4*>(buf + ad.k_lds + i * L::K_ROWS_PER_PASS * L::K_STRIDE) = st.k[i];
   // 4x4 block (rows = 4 keys, columns = 4 value channels) -> 4 rows of V^T
   if constexpr (L::E == 2) {
 #pragma unroll
@@ -190,42 +203,43 @@ __device__ __forceinline__ void store_tile(const Staged<T>& st, const StageAddr<
         o.x = __builtin_amdgcn_perm(s1, s0, 0x07060302u);  // hi halves
         o.y = __builtin_amdgcn_perm(s3, s2, 0x07060302u);
       }
-      *reinterpret_cast<u32x2*>(buf + ad.v_lds[e]) = o;
+      *reinterpret_cast<u32x2*>(buf + ad.v_lds + e * L::VT_STRIDE) = o;
     }
   } else {
-    *reinterpret_cast<u32x4*>(buf + ad.v_lds[0]) = u32x4{st.v[0].x, st.v[1].x, st.v[2].x, st.v[3].x};
-    *reinterpret_cast<u32x4*>(buf + ad.v_lds[1]) = u32x4{st.v[0].y, st.v[1].y, st.v[2].y, st.v[3].y};
-    *reinterpret_cast<u32x4*>(buf + ad.v_lds[2]) = u32x4{st.v[0].z, st.v[1].z, st.v[2].z, st.v[3].z};
-    *reinterpret_cast<u32x4*>(buf + ad.v_lds[3]) = u32x4{st.v[0].w, st.v[1].w, st.v[2].w, st.v[3].w};
+    *reinterpret_cast<u32x4*>(buf + ad.v_lds + 0 * L::VT_STRIDE) = u32x4{st.v[0].x, st.v[1].x, st.v[2].x, st.v[3].x};
+    *reinterpret_cast<u32x4*>(buf + ad.v_lds + 1 * L::VT_STRIDE) = u32x4{st.v[0].y, st.v[1].y, st.v[2].y, st.v[3].y};
+    *reinterpret_cast<u32x4*>(buf + ad.v_lds + 2 * L::VT_STRIDE) = u32x4{st.v[0].z, st.v[1].z, st.v[2].z, st.v[3].z};
+    *reinterpret_cast<u32x4*>(buf + ad.v_lds + 3 * L::VT_STRIDE) = u32x4{st.v[0].w, st.v[1].w, st.v[2].w, st.v[3].w};
   }
-  if (tid < 64) reinterpret_cast<float*>(buf + L::BIAS_OFF)[tid] = st.bias;
+  // every wave writes the same 64 cells (same values): no branch in the loop
+  reinterpret_cast<float*>(buf + L::BIAS_OFF)[tid & 63] = st.bias;
 }
 
-// S^T (32 keys of half kb) x (32 query rows) = K . Q^T
+// S^T (32 keys of half kb) x (32 query rows) = K . Q^T.  `kbase` = this lane's
+// K fragment base inside a stage.
 template <typename T>
-__device__ __forceinline__ f32x16 qk_half(const char* buf, const int (&k_off)[2][8][2],
+__device__ __forceinline__ f32x16 qk_half(const char* buf, int kbase,
                                           const typename Traits<T>::F (&qf)[kD / 16], int kb) {
+  using L = Lay<T>;
   f32x16 s = {};
 #pragma unroll
-  for (int kc = 0; kc < kD / 16; ++kc) {
-    const auto a = lds_frag<T>(buf, k_off[kb][kc][0], k_off[kb][kc][1]);
-    mfma(s, a, qf[kc]);
-  }
+  for (int kc = 0; kc < kD / 16; ++kc)
+    mfma(s, lds_frag<T>(buf, kbase + kb * 32 * L::K_STRIDE + kc * 16 * L::E), qf[kc]);
   return s;
 }
 
-// O^T += V^T (keys of half kb) . P^T
+// O^T += V^T (keys of half kb) . P^T.  `vbase` = this lane's V^T fragment base.
 template <typename T>
-__device__ __forceinline__ void pv_half(const char* buf, const int (&v_off)[4][4][2],
+__device__ __forceinline__ void pv_half(const char* buf, int vbase,
                                         const typename Traits<T>::F (&p)[2], f32x16 (&O)[4],
                                         int kb) {
+  using L = Lay<T>;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int kc2 = 2 * kb + half;
-      const auto a = lds_frag<T>(buf, v_off[db][kc2][0], v_off[db][kc2][1]);
-      mfma(O[db], a, p[half]);
+      mfma(O[db], lds_frag<T>(buf, vbase + db * 32 * L::VT_STRIDE + kc2 * 16 * L::E), p[half]);
     }
 }
 
@@ -321,6 +335,111 @@ __device__ __forceinline__ void softmax_half(const f32x16& s, f32x2 beta, float 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fixed-order stage for bf16 with the cap.
+//
+// Softmax micro-operations of one 32-key half (16 values per lane):
+//   pass 0: t = fma(s, alpha, beta)   1: y = exp2(t)   2: d = fma(y, a, a)
+//   pass 3: r = rcp(d)                4: w = exp2(r)
+//   pass 5: pack pair k to bf16       6: row sum += the packed pair
+// issued as a skewed pipeline: at step tau, pass p works on value tau - 3p,
+// and pair k is packed two steps after its second value is done.
+// ---------------------------------------------------------------------------
+struct SmOp { int pass, idx; };
+struct SmTable { SmOp op[96]; };
+constexpr SmTable make_sm_table() {
+  SmTable t{};
+  int n = 0;
+  constexpr int lag = 3, fe = 4 * lag + 3;
+  for (int tau = 0; n < 96; ++tau) {
+    for (int p = 0; p < 5; ++p) {
+      const int x = tau - p * lag;
+      if (x >= 0 && x < 16) t.op[n++] = SmOp{p, x};
+    }
+    if (tau >= fe && (tau - fe) % 2 == 0 && (tau - fe) / 2 < 8) t.op[n++] = SmOp{5, (tau - fe) / 2};
+    if (tau >= fe + 1 && (tau - fe - 1) % 2 == 0 && (tau - fe - 1) / 2 < 8)
+      t.op[n++] = SmOp{6, (tau - fe - 1) / 2};
+  }
+  return t;
+}
+constexpr SmTable kSm = make_sm_table();
+
+struct SmState {
+  float v[16];
+  bf16x2 pk[8];
+};
+
+__device__ __forceinline__ void sm_op(int pass, int x, SmState& st, const f32x16& s, f32x2 beta,
+                                      float alpha, float den_a, float& rowsum) {
+  switch (pass) {
+    case 0: st.v[x] = __builtin_fmaf(s[x], alpha, x < 8 ? beta.x : beta.y); break;
+    case 1: st.v[x] = __builtin_amdgcn_exp2f(st.v[x]); break;
+    case 2: st.v[x] = __builtin_fmaf(st.v[x], den_a, den_a); break;
+    case 3: st.v[x] = __builtin_amdgcn_rcpf(st.v[x]); break;
+    case 4: st.v[x] = __builtin_amdgcn_exp2f(st.v[x]); break;
+    case 5: {
+      const f32x2 two = {st.v[2 * x], st.v[2 * x + 1]};
+      st.pk[x] = __builtin_convertvector(two, bf16x2);
+      break;
+    }
+    default: {
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      rowsum = __builtin_amdgcn_fdot2_f32_bf16(st.pk[x], ones, rowsum, false);
+      break;
+    }
+  }
+}
+
+// O / rowsum -> output dtype, staged through LDS (XOR-swizzled 16-byte
+// chunks) so the 32 positions x 8 heads x 128 block, contiguous in HBM, is
+// written with coalesced 16-byte stores.  The caller has passed a barrier
+// after the last read of the tile buffers, and another between the staging
+// and the copy.
+template <typename T>
+__device__ __forceinline__ void stage_output(char* smem, const f32x16 (&O)[4], float rowsum,
+                                             int r, int g, int h) {
+  constexpr int E = sizeof(T);
+  constexpr int OUT_ROW = kHeads * kD * E;
+  const float tot = rowsum + __shfl_xor(rowsum, 32);
+  const float inv = 1.0f / tot;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dv = db * 32 + 8 * j + 4 * g;
+      const int byte = (h * kD + dv) * E;
+      const int chunk = byte >> 4, inb = byte & 15;
+      char* dst = smem + r * OUT_ROW + ((chunk ^ r) * 16) + inb;
+      if constexpr (E == 2) {
+        const f32x2 a = {O[db][4 * j + 0] * inv, O[db][4 * j + 1] * inv};
+        const f32x2 c = {O[db][4 * j + 2] * inv, O[db][4 * j + 3] * inv};
+        u32x2 w;
+        w.x = __builtin_bit_cast(unsigned int, __builtin_convertvector(a, bf16x2));
+        w.y = __builtin_bit_cast(unsigned int, __builtin_convertvector(c, bf16x2));
+        *reinterpret_cast<u32x2*>(dst) = w;
+      } else {
+        const f32x4 w = {O[db][4 * j + 0] * inv, O[db][4 * j + 1] * inv,
+                         O[db][4 * j + 2] * inv, O[db][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(dst) = w;
+      }
+    }
+}
+
+template <typename T, int NT>
+__device__ __forceinline__ void copy_output(const char* smem, T* __restrict__ out_block, int tid) {
+  constexpr int OUT_ROW = kHeads * kD * sizeof(T);
+  char* ob = reinterpret_cast<char*>(out_block);
+  constexpr int CHUNKS_PER_POS = OUT_ROW / 16;
+  constexpr int TOTAL = kBlockPos * CHUNKS_PER_POS;
+#pragma unroll
+  for (int i = 0; i < TOTAL / NT; ++i) {
+    const int id = tid + NT * i;
+    const int rr = id / CHUNKS_PER_POS, c = id % CHUNKS_PER_POS;
+    *reinterpret_cast<u32x4*>(ob + (int64_t)id * 16) =
+        *reinterpret_cast<const u32x4*>(smem + rr * OUT_ROW + ((c ^ rr) * 16));
+  }
+}
+
 template <typename T, bool CAPPED>
 __global__ __launch_bounds__(kThreads, 1)
 void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
@@ -366,51 +485,31 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   }
 
   // ---- loop-invariant addresses -----------------------------------------------
-  StageAddr<T> ad;
-#pragma unroll
-  for (int i = 0; i < L::K_PT; ++i) {
-    const int id = tid + kThreads * i;
-    const int row = id / L::K_CHUNKS, c = id % L::K_CHUNKS;
-    ad.k_lds[i] = row * L::K_ROW + ((c ^ (row & (L::K_CHUNKS - 1))) * 16);
+  StageAddr ad;
+  {
+    // K rows are stored permuted (LDS row kb*32 + rho holds key kb*32 +
+    // key_perm(rho)), so the 8 lanes of an LDS read phase read 8 consecutive
+    // padded rows: distinct banks.
+    const int key = tid / L::K_CHUNKS;
+    const int row = (key & ~31) | key_perm(key & 31);
+    ad.k_lds = row * L::K_STRIDE + (tid % L::K_CHUNKS) * 16;
   }
   {
-    const int dvg = tid & 31, kg = tid >> 5;  // 4x4 block: keys 4kg.., channels 4dvg..
+    // 4x4 block: keys 4kg.., channels 4dvg..; lanes run over kg first so the
+    // transposed stores of a write phase hit distinct banks.
+    const int lane6 = tid & 63, w = tid >> 6;
+    const int kg = (lane6 & 7) | ((w & 1) << 3);
+    const int dvg = ((lane6 >> 3) & 7) | ((w >> 1) << 3);
     ad.v_glb = (kg * 4) * kD * E + dvg * 4 * E;
-    const int byte = kg * 4 * E;
-    const int chunk = byte >> 4, inb = byte & 15;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = dvg * 4 + e;
-      ad.v_lds[e] = L::K_BYTES + d * L::VT_ROW + ((chunk ^ (d & (L::VT_CHUNKS - 1))) * 16) + inb;
-    }
-    const int bh = tid >> 3, pb = (tid >> 2) & 1, cell = tid & 3;
+    ad.v_lds = L::K_BYTES + (dvg * 4) * L::VT_STRIDE + kg * 4 * E;
+    const int bt = tid & 63;
+    const int bh = bt >> 3, pb = (bt >> 2) & 1, cell = bt & 3;
     ad.b_glb = ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell;
   }
-  int k_off[2][8][2];
-  {
-    const int kp = key_perm(r);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int row = kb * 32 + kp;
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const int c = (E == 2) ? (2 * kc + g) : (4 * kc + 2 * g);
-        k_off[kb][kc][0] = row * L::K_ROW + ((c ^ (row & (L::K_CHUNKS - 1))) * 16);
-        k_off[kb][kc][1] = row * L::K_ROW + (((c + 1) ^ (row & (L::K_CHUNKS - 1))) * 16);
-      }
-    }
-  }
-  int v_off[4][4][2];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = db * 32 + r;
-#pragma unroll
-    for (int kc2 = 0; kc2 < 4; ++kc2) {
-      const int c = (E == 2) ? (2 * kc2 + g) : (4 * kc2 + 2 * g);
-      v_off[db][kc2][0] = L::K_BYTES + d * L::VT_ROW + ((c ^ (d & (L::VT_CHUNKS - 1))) * 16);
-      v_off[db][kc2][1] = L::K_BYTES + d * L::VT_ROW + (((c + 1) ^ (d & (L::VT_CHUNKS - 1))) * 16);
-    }
-  }
+  // per-lane A fragment bases inside a stage (lane r reads LDS row r, which
+  // holds key key_perm(r) of the 32-key half)
+  const int kbase = r * L::K_STRIDE + 8 * g * E;
+  const int vbase = L::K_BYTES + r * L::VT_STRIDE + 8 * g * E;
   // bias cells of this lane's row: [h][pb][4 key cells] inside a staged tile
   const int bias_lds = L::BIAS_OFF + (h * 8 + (r >> 4) * 4) * 4;
 
@@ -422,18 +521,20 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   float mrun = -__builtin_inff();
 
   // ---- prologue -----------------------------------------------------------------
+  // Tile indices past the end are clamped to the last tile: the extra loads
+  // and stores go to a buffer nobody reads, and the loop body stays one basic
+  // block for the instruction scheduler.
   Staged<T> st;
+  const int last = n - 1;
   load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, 0, tid, beta_mul);
   store_tile<T>(st, ad, smem, tid);
-  if (n > 1) {
-    load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, 1, tid, beta_mul);
-    store_tile<T>(st, ad, smem + L::STAGE, tid);
-  }
-  if (n > 2) load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, 2, tid, beta_mul);
+  load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(1, last), tid, beta_mul);
+  store_tile<T>(st, ad, smem + L::STAGE, tid);
+  load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(2, last), tid, beta_mul);
   __syncthreads();
 
-  f32x16 S0 = qk_half<T>(smem, k_off, qf, 0);
-  f32x16 S1 = qk_half<T>(smem, k_off, qf, 1);
+  f32x16 S0 = qk_half<T>(smem, kbase, qf, 0);
+  f32x16 S1 = qk_half<T>(smem, kbase, qf, 1);
   F P0[2], P1[2];
   {
     const f32x2 beta = *reinterpret_cast<const f32x2*>(smem + bias_lds);
@@ -441,80 +542,409 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   }
 
   int cur = 0;  // buffer of tile t
-  for (int t = 0; t < n; ++t) {
-    const int nxt = (cur + 1 == NBUF) ? 0 : cur + 1;
-    const bool has_next = t + 1 < n;
-    const char* bcur = smem + cur * L::STAGE;
-    const char* bnxt = smem + nxt * L::STAGE;
-    if constexpr (NBUF == 3) {
-      if (t + 2 < n) {
-        const int b2 = (nxt + 1 == NBUF) ? 0 : nxt + 1;
-        store_tile<T>(st, ad, smem + b2 * L::STAGE, tid);
-        if (t + 3 < n) load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, t + 3, tid, beta_mul);
+  {
+    for (int t = 0; t < last; ++t) {
+      const int nxt = (cur + 1 == NBUF) ? 0 : cur + 1;
+      const char* bcur = smem + cur * L::STAGE;
+      const char* bnxt = smem + nxt * L::STAGE;
+      if constexpr (NBUF == 3) {
+        const int nn = (nxt + 1 == NBUF) ? 0 : nxt + 1;
+        store_tile<T>(st, ad, smem + nn * L::STAGE, tid);
+        load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(t + 3, last), tid, beta_mul);
       }
-    }
-    // Stage X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1)
-    pv_half<T>(bcur, v_off, P0, O, 0);
-    if (has_next) S0 = qk_half<T>(bnxt, k_off, qf, 0);
-    {
-      const f32x2 beta = *reinterpret_cast<const f32x2*>(bcur + bias_lds + 8);
-      softmax_half<T, CAPPED>(S1, beta, alpha, den_a, mrun, rowsum, O, P1);
-    }
-    // Stage Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0)
-    pv_half<T>(bcur, v_off, P1, O, 1);
-    if (has_next) {
-      S1 = qk_half<T>(bnxt, k_off, qf, 1);
-      const f32x2 beta = *reinterpret_cast<const f32x2*>(bnxt + bias_lds);
-      softmax_half<T, CAPPED>(S0, beta, alpha, den_a, mrun, rowsum, O, P0);
-    }
-    if constexpr (NBUF == 2) {
-      __syncthreads();  // every wave is done with tile t
-      if (t + 2 < n) {
+      // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1)
+      pv_half<T>(bcur, vbase, P0, O, 0);
+      S0 = qk_half<T>(bnxt, kbase, qf, 0);
+      {
+        const f32x2 beta = *reinterpret_cast<const f32x2*>(bcur + bias_lds + 8);
+        softmax_half<T, CAPPED>(S1, beta, alpha, den_a, mrun, rowsum, O, P1);
+      }
+      // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0)
+      pv_half<T>(bcur, vbase, P1, O, 1);
+      S1 = qk_half<T>(bnxt, kbase, qf, 1);
+      {
+        const f32x2 beta = *reinterpret_cast<const f32x2*>(bnxt + bias_lds);
+        softmax_half<T, CAPPED>(S0, beta, alpha, den_a, mrun, rowsum, O, P0);
+      }
+      if constexpr (NBUF == 2) {
+        __syncthreads();  // every wave is done with tile t: its buffer is free
         store_tile<T>(st, ad, smem + cur * L::STAGE, tid);
-        if (t + 3 < n) load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, t + 3, tid, beta_mul);
+        load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(t + 3, last), tid, beta_mul);
       }
+      __syncthreads();
+      cur = nxt;
     }
-    __syncthreads();
-    cur = nxt;
   }
+  // last tile: PV of both halves and the softmax of its second half
+  {
+    const char* bcur = smem + cur * L::STAGE;
+    pv_half<T>(bcur, vbase, P0, O, 0);
+    const f32x2 beta = *reinterpret_cast<const f32x2*>(bcur + bias_lds + 8);
+    softmax_half<T, CAPPED>(S1, beta, alpha, den_a, mrun, rowsum, O, P1);
+    pv_half<T>(bcur, vbase, P1, O, 1);
+  }
+  __syncthreads();  // the output staging below reuses the tile buffers
 
-  // ---- epilogue: O / rowsum, stage in LDS, coalesced store -------------------------
-  const float tot = rowsum + __shfl_xor(rowsum, 32);
-  const float inv = 1.0f / tot;
+  stage_output<T>(smem, O, rowsum, r, g, h);
+  __syncthreads();
+  copy_output<T, kThreads>(smem, out + ((int64_t)b * S + pos0) * kHeads * kD, tid);
+}
+
+// ===========================================================================
+// gfx950 path for bf16 inputs with the cap.
+//
+// LDS (bytes): V tiles at s * 16 KiB (s = 0..2), K tiles at 48 KiB + s * 16
+// KiB, bias cells at 96 KiB + s * 256.  Tiles arrive straight from HBM with
+// global_load_lds_dwordx4 (16 bytes per lane, no register staging); each lane
+// fetches the chunk that belongs at its LDS slot, which applies the layouts:
+//   * K: LDS row kb*32 + rho holds key kb*32 + key_perm(rho); its 16-byte
+//     chunk c sits at c ^ (row & 15), so the 16 lanes of an LDS read phase
+//     (16 consecutive rows, same chunk) hit distinct banks;
+//   * V: row-major as in HBM, 32-byte slot u of key row j at
+//     u ^ (j & 3) ^ ((u & 1) << 2).
+//     The PV A operand (8 consecutive keys of one value channel) comes from
+//     two ds_read_b64_tr_b16: in each 16-lane group, lane a + 4k returns
+//     element b of its 8 bytes to lane 4a + b as element k, so lane s reading
+//     key row s/4, channels 4(s%4).. delivers 4 keys of one channel per lane;
+//     the 4 rows x 32 bytes of a group land in distinct banks, and the two
+//     groups of a half-wave (odd and even slots) in different bank halves.
+// The main loop is unrolled three times so every LDS address is a
+// loop-invariant register plus an immediate offset.
+// ===========================================================================
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+namespace fp {
+constexpr int NBUF = 3;
+constexpr int ROW = kD * 2;            // bytes per K or V row
+constexpr int TILE = kTileKeys * ROW;  // 16 KiB
+constexpr int V0 = 0;
+constexpr int K0 = NBUF * TILE;
+constexpr int B0 = 2 * NBUF * TILE;
+constexpr int SMEM = B0 + NBUF * 256;
+static_assert(SMEM >= kBlockPos * kHeads * kD * 2, "output staging fits in the tile buffers");
+}  // namespace fp
+
+// MFMA order inside a stage: PV(db 0..2, half 0), QK(kc 0..7), PV(db 3, half
+// 0), PV(db 0..3, half 1).  The QK^T chain ends mid-stage, long before the
+// next stage's softmax reads it, and the first three MFMAs read V only.
+__device__ __forceinline__ constexpr bool slot_is_qk(int j) { return j >= 3 && j <= 10; }
+__device__ __forceinline__ constexpr int slot_kc(int j) { return j - 3; }
+__device__ __forceinline__ constexpr int slot_db(int j) { return j < 3 ? j : (j == 11 ? 3 : j - 12); }
+__device__ __forceinline__ constexpr int slot_half(int j) { return j < 12 ? 0 : 1; }
+
+// A operand of K^T tiles: 8 dk values of key row kb*32 + r.
+template <int S>
+__device__ __forceinline__ bf16x8 kfrag(const char* smem, const int (&kro)[8], int kb, int kc) {
+  return *reinterpret_cast<const bf16x8*>(smem + kro[kc] + S * fp::TILE + kb * 32 * fp::ROW);
+}
+// A operand of V^T tiles: 8 keys (16-key chunk kc2) of one value channel.
+template <int S>
+__device__ __forceinline__ bf16x8 vfrag(const char* smem, const int (&vro)[4], int db, int kc2) {
+  const char* p = smem + vro[db] + S * fp::TILE + kc2 * 16 * fp::ROW;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * fp::ROW));
+  bf16x8 f;
+  __builtin_memcpy(&f, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&f) + 8, &hi, 8);
+  return f;
+}
+
+// One stage: for each of the HPW heads of the wave, 16 MFMAs (PV of half KB
+// of the tile in V stage SV, QK^T of half KB of the tile in K stage SK) woven
+// with the softmax of `ssm` into `pout`.  Each A fragment read from LDS feeds
+// the MFMAs of all HPW heads.  ring[] holds A fragments three slots ahead;
+// the last three slots fetch the first three fragments of the following
+// stage (PV on half NKB of V stage NSV).
+template <int HPW, int SV, int SK, int KB, int NSV, int NKB>
+__device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8], const int (&vro)[4],
+                                       const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][4],
+                                       f32x16 (&sout)[HPW], const bf16x8 (&pin)[HPW][2],
+                                       const f32x16 (&ssm)[HPW], const f32x2 (&beta)[HPW],
+                                       float alpha, float den_a, float (&rowsum)[HPW],
+                                       bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4]) {
+  SmState sm[HPW];
+  f32x16 acc[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) acc[hh] = f32x16{};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int jn = j + 3;
+    if (jn < 16) {
+      ring[jn & 3] = slot_is_qk(jn) ? kfrag<SK>(smem, kro, KB, slot_kc(jn))
+                                    : vfrag<SV>(smem, vro, slot_db(jn), 2 * KB + slot_half(jn));
+    } else {
+      ring[jn & 3] = vfrag<NSV>(smem, vro, slot_db(jn - 16), 2 * NKB);
+    }
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      if (slot_is_qk(j)) {
+        mfma(acc[hh], ring[j & 3], qf[hh][slot_kc(j)]);
+      } else {
+        mfma(O[hh][slot_db(j)], ring[j & 3], pin[hh][slot_half(j)]);
+      }
+#pragma unroll
+      for (int u = 0; u < 6; ++u)
+        sm_op(kSm.op[6 * j + u].pass, kSm.op[6 * j + u].idx, sm[hh], ssm[hh], beta[hh], alpha,
+              den_a, rowsum[hh]);
+    }
+    // inside the slot: the MFMA first, then the LDS reads, then the VALU work
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6 * HPW, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    sout[hh] = acc[hh];
+    bf16x8 f0, f1;
+    __builtin_memcpy(&f0, &sm[hh].pk[0], 16);
+    __builtin_memcpy(&f1, &sm[hh].pk[4], 16);
+    pout[hh][0] = f0;
+    pout[hh][1] = f1;
+  }
+}
+
+template <int HPW>
+struct FastCtx {
+  static constexpr int NW = kHeads / HPW;   // waves per workgroup
+  static constexpr int LPW = 16 / NW;       // direct loads per wave per tile and operand
+  const char* kb_ptr;   // K of this batch item
+  const char* vb_ptr;   // V of this batch item
+  const float* bias_b;  // compact bias of this batch item
+  int64_t b_glb;        // this thread's bias cell (tile 0)
+  int goff_k[LPW], goff_v[LPW];  // per-lane source offsets of the direct loads
+  int wave;             // wave index (uniform)
+  int bt;               // bias cell written by this thread
+  float beta_mul;
+};
+
+// Direct HBM -> LDS copy of K and V of tile t into stage S (2 * LPW loads per
+// wave, 1 KiB each).
+template <int HPW, int S>
+__device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW>& c, int t) {
+  constexpr int LPW = FastCtx<HPW>::LPW;
+  const char* kt = c.kb_ptr + (int64_t)t * fp::TILE;
+  const char* vt = c.vb_ptr + (int64_t)t * fp::TILE;
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtin; the host pass sees an empty body
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int slot = (LPW * c.wave + j) * 1024;
+    __builtin_amdgcn_global_load_lds(kt + c.goff_k[j], (lds_void*)(smem + fp::K0 + S * fp::TILE + slot), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vt + c.goff_v[j], (lds_void*)(smem + fp::V0 + S * fp::TILE + slot), 16, 0, 0);
+  }
+#else
+  (void)kt; (void)vt; (void)smem;
+#endif
+}
+
+template <int HPW>
+__device__ __forceinline__ float load_bias(const FastCtx<HPW>& c, int t) {
+  return c.bias_b[c.b_glb + t * 4] * c.beta_mul;
+}
+
+template <int HPW, int S>
+__device__ __forceinline__ void store_bias(char* smem, const FastCtx<HPW>& c, float v) {
+  // every wave writes the same 64 cells (same values)
+  reinterpret_cast<float*>(smem + fp::B0 + S * 256)[c.bt] = v;
+}
+
+// Wait for this wave's direct loads (and the bias load), then the workgroup
+// barrier that publishes them.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+}
+
+template <int HPW, int S>
+__device__ __forceinline__ void read_beta(const char* smem, const int (&bias_l)[HPW], int half,
+                                          f32x2 (&beta)[HPW]) {
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    beta[hh] = *reinterpret_cast<const f32x2*>(smem + bias_l[hh] + S * 256 + 8 * half);
+}
+
+// One pipelined iteration for tile t in stage C.
+template <int HPW, int C>
+__device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW>& c, int t, int last,
+                                          const int (&kro)[8], const int (&vro)[4],
+                                          const int (&bias_l)[HPW], const bf16x8 (&qf)[HPW][8],
+                                          f32x16 (&O)[HPW][4], f32x16 (&S0)[HPW],
+                                          f32x16 (&S1)[HPW], bf16x8 (&P0)[HPW][2],
+                                          bf16x8 (&P1)[HPW][2], float& breg, float alpha,
+                                          float den_a, float (&rowsum)[HPW], bf16x8 (&ring)[4]) {
+  constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
+  // tile t+2 into the stage that held tile t-1 (clamped past the end: the
+  // copy lands in a stage nobody reads again)
+  issue_tile<HPW, NN>(smem, c, min(t + 2, last));
+  store_bias<HPW, NN>(smem, c, breg);
+  breg = load_bias(c, min(t + 3, last));
+  f32x2 beta[HPW];
+  // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
+  read_beta<HPW, C>(smem, bias_l, 1, beta);
+  fstage<HPW, C, NXT, 0, C, 1>(smem, kro, vro, qf, O, S0, P0, S1, beta, alpha, den_a, rowsum, P1, ring);
+  // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
+  read_beta<HPW, NXT>(smem, bias_l, 0, beta);
+  fstage<HPW, C, NXT, 1, NXT, 0>(smem, kro, vro, qf, O, S1, P1, S0, beta, alpha, den_a, rowsum, P0, ring);
+  tile_barrier();
+}
+
+// Last tile (stage C): PV of both halves and the softmax of its second half.
+template <int HPW, int C>
+__device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[4],
+                                          const int (&bias_l)[HPW], f32x16 (&O)[HPW][4],
+                                          const f32x16 (&S1)[HPW], const bf16x8 (&P0)[HPW][2],
+                                          float alpha, float den_a, float (&rowsum)[HPW]) {
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int dv = db * 32 + 8 * j + 4 * g;
-      const int byte = (h * kD + dv) * E;
-      const int chunk = byte >> 4, inb = byte & 15;
-      char* dst = smem + r * L::OUT_ROW + ((chunk ^ r) * 16) + inb;
-      if constexpr (E == 2) {
-        const f32x2 a = {O[db][4 * j + 0] * inv, O[db][4 * j + 1] * inv};
-        const f32x2 c = {O[db][4 * j + 2] * inv, O[db][4 * j + 3] * inv};
-        bf16x2 lo = __builtin_convertvector(a, bf16x2);
-        bf16x2 hi = __builtin_convertvector(c, bf16x2);
-        u32x2 w;
-        w.x = __builtin_bit_cast(unsigned int, lo);
-        w.y = __builtin_bit_cast(unsigned int, hi);
-        *reinterpret_cast<u32x2*>(dst) = w;
-      } else {
-        const f32x4 w = {O[db][4 * j + 0] * inv, O[db][4 * j + 1] * inv,
-                         O[db][4 * j + 2] * inv, O[db][4 * j + 3] * inv};
-        *reinterpret_cast<f32x4*>(dst) = w;
-      }
-    }
-  __syncthreads();
-  char* ob = reinterpret_cast<char*>(out + ((int64_t)b * S + pos0) * kHeads * kD);
-  constexpr int CHUNKS_PER_POS = L::OUT_ROW / 16;
-  constexpr int TOTAL = kBlockPos * CHUNKS_PER_POS;
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 a = vfrag<C>(smem, vro, db, half);
 #pragma unroll
-  for (int i = 0; i < TOTAL / kThreads; ++i) {
-    const int id = tid + kThreads * i;
-    const int rr = id / CHUNKS_PER_POS, c = id % CHUNKS_PER_POS;
-    *reinterpret_cast<u32x4*>(ob + (int64_t)id * 16) =
-        *reinterpret_cast<const u32x4*>(smem + rr * L::OUT_ROW + ((c ^ rr) * 16));
+      for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P0[hh][half]);
+    }
+  f32x2 beta[HPW];
+  read_beta<HPW, C>(smem, bias_l, 1, beta);
+  bf16x8 P1[HPW][2];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) softmax_capped<__bf16>(S1[hh], beta[hh], alpha, den_a, rowsum[hh], P1[hh]);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 a = vfrag<C>(smem, vro, db, 2 + half);
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P1[hh][half]);
+    }
+}
+
+template <int HPW>
+__global__ __launch_bounds__(64 * (kHeads / HPW), 1)
+void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                       const __bf16* __restrict__ v, const float* __restrict__ bias,
+                                       __bf16* __restrict__ out, int S, int64_t bias_batch_stride,
+                                       int bias_group, float alpha, float beta_mul, float den_a) {
+  constexpr int NT = 64 * (kHeads / HPW);
+  constexpr int LPW = FastCtx<HPW>::LPW;
+  __shared__ __attribute__((aligned(16))) char smem[fp::SMEM];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r = lane & 31;
+  const int g = lane >> 5;
+  const int b = blockIdx.y;
+  const int pos0 = blockIdx.x * kBlockPos;
+  const int P = S >> 4;
+  const int n = S / kTileKeys;
+  const int last = n - 1;
+
+  FastCtx<HPW> c;
+  c.kb_ptr = reinterpret_cast<const char*>(k + (int64_t)b * S * kD);
+  c.vb_ptr = reinterpret_cast<const char*>(v + (int64_t)b * S * kD);
+  c.bias_b = bias + (int64_t)(b / bias_group) * bias_batch_stride;
+  c.beta_mul = beta_mul;
+  c.wave = __builtin_amdgcn_readfirstlane(w);
+  c.bt = tid & 63;
+  {
+    const int bh = c.bt >> 3, pb = (c.bt >> 2) & 1, cell = c.bt & 3;
+    c.b_glb = ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell;
   }
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int qs = (LPW * w + j) * 64 + lane;  // 16-byte slot of this lane in a tile
+    const int row = qs >> 4, pc = qs & 15;
+    const int key = (row & 32) | key_perm(row & 31);
+    c.goff_k[j] = key * fp::ROW + ((pc ^ (row & 15)) * 16);
+    const int ps = (pc >> 1) ^ (row & 3);     // logical 32-byte slot held by
+    const int sl = ps ^ ((ps & 1) << 2);      // physical slot pc >> 1
+    c.goff_v[j] = row * fp::ROW + (2 * sl + (pc & 1)) * 16;
+  }
+  int kro[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) kro[kc] = fp::K0 + r * fp::ROW + (((2 * kc + g) ^ (r & 15)) * 16);
+  int vro[4];
+  {
+    const int i16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      vro[db] = fp::V0 + (8 * (grp >> 1) + (i16 >> 2)) * fp::ROW +
+                ((((2 * db + (grp & 1)) ^ (i16 >> 2) ^ ((grp & 1) << 2))) * 32) + 8 * (i16 & 3);
+  }
+  int bias_l[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) bias_l[hh] = fp::B0 + ((w * HPW + hh) * 8 + (r >> 4) * 4) * 4;
+
+  bf16x8 qf[HPW][kD / 16];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const char* qrow = reinterpret_cast<const char*>(
+        q + (((int64_t)b * S + pos0 + r) * kHeads + w * HPW + hh) * kD);
+#pragma unroll
+    for (int kc = 0; kc < kD / 16; ++kc) qf[hh][kc] = *reinterpret_cast<const bf16x8*>(qrow + (kc * 16 + 8 * g) * 2);
+  }
+
+  f32x16 O[HPW][4];
+  float rowsum[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    rowsum[hh] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) O[hh][db] = f32x16{};
+  }
+
+  // ---- prologue: tiles 0 and 1 -------------------------------------------------
+  issue_tile<HPW, 0>(smem, c, 0);
+  issue_tile<HPW, 1>(smem, c, min(1, last));
+  const float b0v = load_bias(c, 0);
+  const float b1v = load_bias(c, min(1, last));
+  float breg = load_bias(c, min(2, last));
+  store_bias<HPW, 0>(smem, c, b0v);
+  store_bias<HPW, 1>(smem, c, b1v);
+  tile_barrier();
+
+  f32x16 S0[HPW], S1[HPW];
+  bf16x8 P0[HPW][2], P1[HPW][2];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    S0[hh] = f32x16{};
+    S1[hh] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      mfma(S0[hh], kfrag<0>(smem, kro, 0, kc), qf[hh][kc]);
+      mfma(S1[hh], kfrag<0>(smem, kro, 1, kc), qf[hh][kc]);
+    }
+    softmax_capped<__bf16>(S0[hh], *reinterpret_cast<const f32x2*>(smem + bias_l[hh]), alpha, den_a,
+                           rowsum[hh], P0[hh]);
+  }
+  bf16x8 ring[4];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) ring[j] = vfrag<0>(smem, vro, j, 0);
+
+  // ---- main loop, unrolled over the three stages -------------------------------------
+  int t = 0;
+  while (true) {
+    if (t >= last) break;
+    fast_iter<HPW, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, breg, alpha, den_a, rowsum, ring);
+    ++t;
+    if (t >= last) break;
+    fast_iter<HPW, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, breg, alpha, den_a, rowsum, ring);
+    ++t;
+    if (t >= last) break;
+    fast_iter<HPW, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, breg, alpha, den_a, rowsum, ring);
+    ++t;
+  }
+  switch (last % 3) {
+    case 0: fast_tail<HPW, 0>(smem, vro, bias_l, O, S1, P0, alpha, den_a, rowsum); break;
+    case 1: fast_tail<HPW, 1>(smem, vro, bias_l, O, S1, P0, alpha, den_a, rowsum); break;
+    default: fast_tail<HPW, 2>(smem, vro, bias_l, O, S1, P0, alpha, den_a, rowsum); break;
+  }
+  __syncthreads();  // the output staging reuses the tile buffers
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) stage_output<__bf16>(smem, O[hh], rowsum[hh], r, g, w * HPW + hh);
+  __syncthreads();
+  copy_output<__bf16, NT>(smem, out + ((int64_t)b * S + pos0) * kHeads * kD, tid);
 }
 
 template <typename T, bool CAPPED>
@@ -531,10 +961,18 @@ hipError_t launch_typed(const AttnLaunch& a, hipStream_t stream) {
     den_a = 0.f;
   }
   dim3 grid((unsigned)(a.S / kBlockPos), (unsigned)a.B);
-  hipLaunchKernelGGL((biased_mqa_fwd_kernel<T, CAPPED>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), a.bias, static_cast<T*>(a.out), (int)a.S,
-                     a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+  if constexpr (CAPPED && sizeof(T) == 2) {
+    constexpr int HPW = kFastHeadsPerWave;
+    hipLaunchKernelGGL(biased_mqa_fwd_bf16_capped_kernel<HPW>, grid, dim3(64 * (kHeads / HPW)), 0,
+                       stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), a.bias, static_cast<__bf16*>(a.out),
+                       (int)a.S, a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+  } else {
+    hipLaunchKernelGGL((biased_mqa_fwd_kernel<T, CAPPED>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.bias, static_cast<T*>(a.out), (int)a.S,
+                       a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+  }
   return hipGetLastError();
 }
 

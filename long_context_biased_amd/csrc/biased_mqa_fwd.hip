@@ -707,18 +707,47 @@ __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8], co
   }
 }
 
+// Direct HBM -> LDS copy of 16 bytes per lane: lane l's bytes at base + voff
+// land at LDS address lds + 16 l (base and lds uniform across the wave).  The
+// copy is written out here rather than through the compiler's builtin: the
+// compiler cannot tell which LDS bytes such a copy writes, so after the
+// builtin it makes every later LDS access wait for the copy to finish, which
+// would turn the prefetch of the next tiles into a stall.  The kernel orders
+// the copies itself: each one is waited for (vmcnt 0) and followed by a
+// workgroup barrier before any lane reads its LDS stage.  M0 is read when the
+// copy issues; nothing else in these kernels uses M0.
+__device__ __forceinline__ void lds_copy16(const char* base, int voff, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Direct HBM -> LDS copy of 4 bytes per lane: lane l's float at addr lands at
+// LDS address lds + 4 l.  Same ordering rules as lds_copy16.
+__device__ __forceinline__ void lds_copy4(const float* addr, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(addr), "s"(lds)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 template <int HPW>
 struct FastCtx {
   static constexpr int NW = kHeads / HPW;   // waves per workgroup
   static constexpr int LPW = 16 / NW;       // direct loads per wave per tile and operand
   const char* kb_ptr;   // K of this batch item
   const char* vb_ptr;   // V of this batch item
-  const float* bias_b;  // compact bias of this batch item
-  int64_t b_glb;        // this thread's bias cell (tile 0)
+  const float* bias_lane;  // compact-bias cell that this lane copies for tile 0
   int goff_k[LPW], goff_v[LPW];  // per-lane source offsets of the direct loads
   int wave;             // wave index (uniform)
-  int bt;               // bias cell written by this thread
-  float beta_mul;
+  float beta_mul;       // factor of the bias in the exp2 argument
 };
 
 // Direct HBM -> LDS copy of K and V of tile t into stage S (2 * LPW loads per
@@ -728,28 +757,18 @@ __device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW>& c, in
   constexpr int LPW = FastCtx<HPW>::LPW;
   const char* kt = c.kb_ptr + (int64_t)t * fp::TILE;
   const char* vt = c.vb_ptr + (int64_t)t * fp::TILE;
-#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtin; the host pass sees an empty body
+  const uint32_t lds0 = (uint32_t)(size_t)(lds_void*)smem + S * fp::TILE;
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int slot = (LPW * c.wave + j) * 1024;
-    __builtin_amdgcn_global_load_lds(kt + c.goff_k[j], (lds_void*)(smem + fp::K0 + S * fp::TILE + slot), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vt + c.goff_v[j], (lds_void*)(smem + fp::V0 + S * fp::TILE + slot), 16, 0, 0);
+    const uint32_t slot = lds0 + (uint32_t)((LPW * c.wave + j) * 1024);
+    lds_copy16(kt, c.goff_k[j], slot + fp::K0);
+    lds_copy16(vt, c.goff_v[j], slot + fp::V0);
   }
-#else
-  (void)kt; (void)vt; (void)smem;
-#endif
+  // the tile's 64 compact-bias cells (8 heads x 2 query blocks x 4 key
+  // blocks), one per lane of wave 0
+  if (c.wave == 0) lds_copy4(c.bias_lane + (int64_t)t * 4, (uint32_t)(size_t)(lds_void*)smem + fp::B0 + S * 256);
 }
 
-template <int HPW>
-__device__ __forceinline__ float load_bias(const FastCtx<HPW>& c, int t) {
-  return c.bias_b[c.b_glb + t * 4] * c.beta_mul;
-}
-
-template <int HPW, int S>
-__device__ __forceinline__ void store_bias(char* smem, const FastCtx<HPW>& c, float v) {
-  // every wave writes the same 64 cells (same values)
-  reinterpret_cast<float*>(smem + fp::B0 + S * 256)[c.bt] = v;
-}
 
 // Wait for this wave's direct loads (and the bias load), then the workgroup
 // barrier that publishes them.
@@ -760,10 +779,10 @@ __device__ __forceinline__ void tile_barrier() {
 
 template <int HPW, int S>
 __device__ __forceinline__ void read_beta(const char* smem, const int (&bias_l)[HPW], int half,
-                                          f32x2 (&beta)[HPW]) {
+                                          float beta_mul, f32x2 (&beta)[HPW]) {
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
-    beta[hh] = *reinterpret_cast<const f32x2*>(smem + bias_l[hh] + S * 256 + 8 * half);
+    beta[hh] = *reinterpret_cast<const f32x2*>(smem + bias_l[hh] + S * 256 + 8 * half) * beta_mul;
 }
 
 // One pipelined iteration for tile t in stage C.
@@ -773,20 +792,18 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW>& c, int
                                           const int (&bias_l)[HPW], const bf16x8 (&qf)[HPW][8],
                                           f32x16 (&O)[HPW][4], f32x16 (&S0)[HPW],
                                           f32x16 (&S1)[HPW], bf16x8 (&P0)[HPW][2],
-                                          bf16x8 (&P1)[HPW][2], float& breg, float alpha,
+                                          bf16x8 (&P1)[HPW][2], float alpha,
                                           float den_a, float (&rowsum)[HPW], bf16x8 (&ring)[4]) {
   constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
   // tile t+2 into the stage that held tile t-1 (clamped past the end: the
   // copy lands in a stage nobody reads again)
   issue_tile<HPW, NN>(smem, c, min(t + 2, last));
-  store_bias<HPW, NN>(smem, c, breg);
-  breg = load_bias(c, min(t + 3, last));
   f32x2 beta[HPW];
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
-  read_beta<HPW, C>(smem, bias_l, 1, beta);
+  read_beta<HPW, C>(smem, bias_l, 1, c.beta_mul, beta);
   fstage<HPW, C, NXT, 0, C, 1>(smem, kro, vro, qf, O, S0, P0, S1, beta, alpha, den_a, rowsum, P1, ring);
   // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
-  read_beta<HPW, NXT>(smem, bias_l, 0, beta);
+  read_beta<HPW, NXT>(smem, bias_l, 0, c.beta_mul, beta);
   fstage<HPW, C, NXT, 1, NXT, 0>(smem, kro, vro, qf, O, S1, P1, S0, beta, alpha, den_a, rowsum, P0, ring);
   tile_barrier();
 }
@@ -796,7 +813,8 @@ template <int HPW, int C>
 __device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[4],
                                           const int (&bias_l)[HPW], f32x16 (&O)[HPW][4],
                                           const f32x16 (&S1)[HPW], const bf16x8 (&P0)[HPW][2],
-                                          float alpha, float den_a, float (&rowsum)[HPW]) {
+                                          float alpha, float beta_mul, float den_a,
+                                          float (&rowsum)[HPW]) {
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -806,7 +824,7 @@ __device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[4],
       for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P0[hh][half]);
     }
   f32x2 beta[HPW];
-  read_beta<HPW, C>(smem, bias_l, 1, beta);
+  read_beta<HPW, C>(smem, bias_l, 1, beta_mul, beta);
   bf16x8 P1[HPW][2];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) softmax_capped<__bf16>(S1[hh], beta[hh], alpha, den_a, rowsum[hh], P1[hh]);
@@ -843,13 +861,13 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   FastCtx<HPW> c;
   c.kb_ptr = reinterpret_cast<const char*>(k + (int64_t)b * S * kD);
   c.vb_ptr = reinterpret_cast<const char*>(v + (int64_t)b * S * kD);
-  c.bias_b = bias + (int64_t)(b / bias_group) * bias_batch_stride;
   c.beta_mul = beta_mul;
   c.wave = __builtin_amdgcn_readfirstlane(w);
-  c.bt = tid & 63;
   {
-    const int bh = c.bt >> 3, pb = (c.bt >> 2) & 1, cell = c.bt & 3;
-    c.b_glb = ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell;
+    // bias cell of lane l: head l>>3, query block (l>>2)&1, key block l&3
+    const int bh = lane >> 3, pb = (lane >> 2) & 1, cell = lane & 3;
+    c.bias_lane = bias + (int64_t)(b / bias_group) * bias_batch_stride +
+                  ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell;
   }
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
@@ -897,11 +915,6 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   // ---- prologue: tiles 0 and 1 -------------------------------------------------
   issue_tile<HPW, 0>(smem, c, 0);
   issue_tile<HPW, 1>(smem, c, min(1, last));
-  const float b0v = load_bias(c, 0);
-  const float b1v = load_bias(c, min(1, last));
-  float breg = load_bias(c, min(2, last));
-  store_bias<HPW, 0>(smem, c, b0v);
-  store_bias<HPW, 1>(smem, c, b1v);
   tile_barrier();
 
   f32x16 S0[HPW], S1[HPW];
@@ -915,8 +928,8 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
       mfma(S0[hh], kfrag<0>(smem, kro, 0, kc), qf[hh][kc]);
       mfma(S1[hh], kfrag<0>(smem, kro, 1, kc), qf[hh][kc]);
     }
-    softmax_capped<__bf16>(S0[hh], *reinterpret_cast<const f32x2*>(smem + bias_l[hh]), alpha, den_a,
-                           rowsum[hh], P0[hh]);
+    softmax_capped<__bf16>(S0[hh], *reinterpret_cast<const f32x2*>(smem + bias_l[hh]) * beta_mul, alpha,
+                           den_a, rowsum[hh], P0[hh]);
   }
   bf16x8 ring[4];
 #pragma unroll
@@ -926,19 +939,19 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   int t = 0;
   while (true) {
     if (t >= last) break;
-    fast_iter<HPW, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, breg, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
     if (t >= last) break;
-    fast_iter<HPW, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, breg, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
     if (t >= last) break;
-    fast_iter<HPW, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, breg, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
   }
   switch (last % 3) {
-    case 0: fast_tail<HPW, 0>(smem, vro, bias_l, O, S1, P0, alpha, den_a, rowsum); break;
-    case 1: fast_tail<HPW, 1>(smem, vro, bias_l, O, S1, P0, alpha, den_a, rowsum); break;
-    default: fast_tail<HPW, 2>(smem, vro, bias_l, O, S1, P0, alpha, den_a, rowsum); break;
+    case 0: fast_tail<HPW, 0>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    case 1: fast_tail<HPW, 1>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    default: fast_tail<HPW, 2>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
   }
   __syncthreads();  // the output staging reuses the tile buffers
 #pragma unroll

@@ -11,7 +11,7 @@ Prints ONE JSON line: attention TFLOP/s over the whole step (FLOPs =
 kernel (the attention) from HIP events on its own stream, and the CPU oracle
 timed on a bounded sample (one of the 9 layers) on this host's cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-mib N]
 """
 
 from __future__ import annotations
@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=9)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the measurement, run 3 plain device-to-device copies of this "
+                         "many MiB (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -187,6 +190,18 @@ def main():
         f"(median {np.median(attn_ms) * 1e3:.1f}, p95 {np.percentile(attn_ms, 95) * 1e3:.1f}) "
         f"= {achieved:.1f} TFLOP/s; projection avg {proj_avg * 1e3:.1f} us = "
         f"{pb / (proj_avg * 1e-3) / 1e9:.0f} GB/s")
+
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {args.copy_mib} MiB")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -5,16 +5,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-# Query positions checked at full size: tile and bias-cell edges, the
-# variant rows, the end, plus a few seeded random positions.
-def sample_rows(S, seed=0, extra=12):
-    base = [0, 1, 15, 16, 31, 32, 63, 64, 65, S // 2 - 1, S // 2, S - 65, S - 64, S - 17,
-            S - 16, S - 1]
-    if S > 4101:
-        base += list(range(4090, 4102))
-    rng = np.random.Generator(np.random.PCG64(seed + S))
-    base += rng.integers(0, S, size=extra).tolist()
-    return np.array(sorted(set(int(r) for r in base if 0 <= r < S)))
+from parity import sample_rows  # noqa: F401  (re-exported for the GPU tests)
 
 
 def to_gpu(a: np.ndarray, device="cuda") -> torch.Tensor:

@@ -52,3 +52,15 @@ def projection_ok(got, ref):
     max_abs, rel = stats(got, ref)
     scale = max(1e-30, float(np.max(np.abs(ref))))
     return (rel <= PROJ_TOL["rel_l2"] and max_abs <= PROJ_TOL["max_abs_rel"] * scale), max_abs, rel
+
+
+def sample_rows(S, seed=0, extra=12):
+    """Query positions checked at full size: tile and bias-cell edges, the
+    variant rows, the end, plus a few seeded random positions."""
+    base = [0, 1, 15, 16, 31, 32, 63, 64, 65, S // 2 - 1, S // 2, S - 65, S - 64, S - 17,
+            S - 16, S - 1]
+    if S > 4101:
+        base += list(range(4090, 4102))
+    rng = np.random.Generator(np.random.PCG64(seed + S))
+    base += rng.integers(0, S, size=extra).tolist()
+    return np.array(sorted(set(int(r) for r in base if 0 <= r < S)))

@@ -128,6 +128,77 @@ void pair_bias_project_kernel(const T* __restrict__ pair, const T* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs with C a multiple of 32: the projection as a skinny matrix
+// product on the matrix cores, D = W^T . pair^T per 16 cells, with the
+// 16x16x32 bf16 MFMA (float32 accumulation):
+//   * A (16 x 32) = W^T for one 32-channel step: row m = head (rows 8..15
+//     are zero), lane l holds row l % 16, channels 8 (l >> 4) .. + 7;
+//     the C / 32 fragments stay in registers for the whole kernel;
+//   * B (32 x 16) = pair^T: column n = cell, lane l holds cell l % 16,
+//     channels 8 (l >> 4) .. + 7 of the step -- one 16-byte load per lane
+//     straight from HBM (each cell row is C * 2 contiguous bytes);
+//   * D (16 x 16): lane l holds cell l % 16, heads 4 (l >> 4) .. + 3 (lanes
+//     32..63 hold the zero rows and store nothing).
+// A wave takes 64 cells per step: it issues the loads of all its fragments
+// at once (4 cell groups x C / 32 steps) and then runs the MFMAs, so every
+// wave keeps 64 * C * 2 bytes in flight; the pass is bound by HBM.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaMaxC = 256;
+
+template <int NKS>  // C / 32
+__global__ __launch_bounds__(kThreads)
+void pair_bias_project_mfma_kernel(const __bf16* __restrict__ pair, const __bf16* __restrict__ weight,
+                                   float* __restrict__ bias, int64_t n_cells_per_item,
+                                   int64_t n_items) {
+  constexpr int C = NKS * 32;
+  constexpr int G = 4;  // 16-cell groups per wave step
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+
+  bf16x8_t a[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      a[ks][i] = col < kH ? weight[(ks * 32 + 8 * kg + i) * kH + col] : (__bf16)0.0f;
+  }
+
+  const int64_t total = n_cells_per_item * n_items;
+  const int64_t n_steps = (total + 63) / 64;
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+  for (int64_t step = (int64_t)blockIdx.x * kWaves + wave; step < n_steps; step += n_waves) {
+    const int64_t cell0 = step * 64;
+    bf16x8_t b[G][NKS];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      int64_t cell = cell0 + g * 16 + col;
+      cell = cell < total ? cell : total - 1;  // past the end: load a valid cell, store nothing
+      const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(pair + cell * C + 8 * kg);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) b[g][ks] = src[ks * 4];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b[g][ks], d, 0, 0, 0);
+      const int64_t cell = cell0 + g * 16 + col;
+      if (kg < 2 && cell < total) {
+        const int64_t item = cell / n_cells_per_item;
+        const int64_t pr = cell - item * n_cells_per_item;
+        float* dst = bias + (item * kH + 4 * kg) * n_cells_per_item + pr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i * n_cells_per_item] = d[i];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pair_bias_project(const void* pair, const void* weight, float* bias,
@@ -138,7 +209,23 @@ hipError_t launch_pair_bias_project(const void* pair, const void* weight, float*
   int64_t blocks = (steps + kWaves - 1) / kWaves;
   const int64_t max_blocks = 256 * 8;  // 8 workgroups per CU is plenty for a stream
   if (blocks > max_blocks) blocks = max_blocks;
-  if (dtype == ABG_BF16) {
+  if (dtype == ABG_BF16 && C % 32 == 0 && C <= kMfmaMaxC) {
+    const int64_t wsteps = (cells * Bp + 63) / 64;
+    int64_t mblocks = (wsteps + kWaves - 1) / kWaves;
+    if (mblocks > 65536) mblocks = 65536;
+    const __bf16* p = static_cast<const __bf16*>(pair);
+    const __bf16* w = static_cast<const __bf16*>(weight);
+    switch (C / 32) {
+      case 1: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<1>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+      case 2: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<2>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+      case 3: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<3>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+      case 4: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<4>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+      case 5: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<5>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+      case 6: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<6>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+      case 7: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<7>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+      default: hipLaunchKernelGGL(pair_bias_project_mfma_kernel<8>, dim3((unsigned)mblocks), dim3(kThreads), 0, stream, p, w, bias, cells, Bp); break;
+    }
+  } else if (dtype == ABG_BF16) {
     hipLaunchKernelGGL(pair_bias_project_kernel<__bf16>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, static_cast<const __bf16*>(pair), static_cast<const __bf16*>(weight),
                        bias, cells, Bp, (int)C);

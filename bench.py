@@ -9,9 +9,10 @@ one stream with every input already resident in HBM.
 Prints ONE JSON line: attention TFLOP/s over the whole step (FLOPs =
 4*B*Hq*S^2*d per layer, non-causal QK^T + PV), the roofline of the dominant
 kernel (the attention) from HIP events on its own stream, and the CPU oracle
-timed on a bounded sample (one of the 9 layers) on this host's cores.
+timed on a bounded sample (3 of the 9 layers by default) on this host's cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-mib N]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--cpu-layers N]
+                    [--copy-mib N]
 """
 
 from __future__ import annotations
@@ -72,9 +73,10 @@ def load_traffic(per_launch_flops_unit):
         return None
 
 
-def cpu_baseline(layer):
-    """The oracle (unchanged) on one full layer: projection + all 8192 x 8
-    output rows, timed on this host's cores."""
+def cpu_baseline(host_layers):
+    """The oracle (unchanged) on a bounded sample of the workload: the first
+    layers (projection + all 8192 x 8 output rows each), timed on this host's
+    cores."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -82,14 +84,16 @@ def cpu_baseline(layer):
     except Exception:  # pragma: no cover
         threads = 1
     t0 = time.perf_counter()
-    bias = oracle.project_pair_bias(layer.pair, layer.weight)
-    oracle.attention(layer.q, layer.k, layer.v, bias, scale=layer.scale, cap=layer.cap)
+    for layer in host_layers:
+        bias = oracle.project_pair_bias(layer.pair, layer.weight)
+        oracle.attention(layer.q, layer.k, layer.v, bias, scale=layer.scale, cap=layer.cap)
     dt = time.perf_counter() - t0
-    fl = attn_flops(layer.B, layer.S)
+    L0 = host_layers[0]
+    fl = attn_flops(L0.B, L0.S) * len(host_layers)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"1 of the 9 layers (projection + all {layer.S} positions x 8 heads), "
-                       f"float64 numpy, {dt:.1f} s wall; BLAS threads = cores")}
+            "sample": (f"{len(host_layers)} of the 9 layers (projection + all {L0.S} positions x "
+                       f"8 heads each), float64 numpy, {dt:.1f} s wall; BLAS threads = cores")}
 
 
 def main():
@@ -99,6 +103,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=9)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=3,
+                    help="layers in the oracle's timed sample (about 4-5 s each on 16 cores)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 3 plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -124,11 +130,11 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     t0 = time.perf_counter()
-    layers, host0 = [], None
+    layers, host = [], []
     for li in range(n_layers):
         L = workloads.make_layer("full", layer=li)
-        if li == 0:
-            host0 = L
+        if li < max(1, args.cpu_layers):
+            host.append(L)
         t = {n: to_gpu(getattr(L, n)) for n in ("q", "k", "v", "pair", "weight")}
         P = L.S // 16
         t["bias"] = torch.empty((8, P, P), dtype=torch.float32, device=dev)
@@ -136,6 +142,7 @@ def main():
         layers.append(t)
     torch.cuda.synchronize()
     log(f"inputs: {n_layers} layers generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    host0 = host[0]
     S = host0.S
     P = S // 16
     scale = host0.scale
@@ -205,8 +212,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on one layer ...")
-        cpu = cpu_baseline(host0)
+        log(f"cpu baseline: oracle on {len(host)} layer(s) ...")
+        cpu = cpu_baseline(host[:max(1, args.cpu_layers)])
         log(f"cpu baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
     rec = {

@@ -91,6 +91,12 @@ SMALL = [
     (4, 256, "bf16", 1.5, 1.0, 3.0, 2),
     (1, 1024, "f32", 5.0, 1.5, 2.0, None),
     (1, 1024, "bf16", 0.0, 0.5, 1.0, None),
+    # bf16 with the cap at 3, 6 and 9 tiles: the last tile lands in each of
+    # the three rotating LDS stages (1, 2, 4 and 16 tiles above cover the rest)
+    (2, 192, "bf16", 5.0, 1.0, 2.0, None),
+    (1, 384, "bf16", 5.0, 1.0, 2.0, None),
+    (1, 576, "bf16", 2.0, 0.09, 1.0, None),
+    (1, 448, "f32", 5.0, 1.0, 2.0, None),
 ]
 
 

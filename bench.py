@@ -7,12 +7,12 @@ heads, 1 K/V head, d=128, bf16 inputs, fp32 accumulation), back to back on
 one stream with every input already resident in HBM.
 
 Prints ONE JSON line: attention TFLOP/s over the whole step (FLOPs =
-4*B*Hq*S^2*d per layer, non-causal QK^T + PV), the roofline of the dominant
+2*B*Hq*S^2*(Dk + Dv) per layer, non-causal QK^T + PV), the roofline of the dominant
 kernel (the attention) from HIP events on its own stream, and the CPU oracle
 timed on a bounded sample (3 of the 9 layers by default) on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--cpu-layers N]
-                    [--copy-mib N]
+                    [--dv 128|192] [--copy-mib N]
 """
 
 from __future__ import annotations
@@ -39,8 +39,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attn_flops(B, S, H=8, D=128):
-    return 4.0 * B * H * S * S * D
+def attn_flops(B, S, H=8, Dk=128, Dv=128):
+    """QK^T + PV multiply-adds, non-causal: 2 B H S^2 (Dk + Dv)."""
+    return 2.0 * B * H * S * S * (Dk + Dv)
 
 
 def proj_bytes(P, C, H=8, elem=2):
@@ -89,7 +90,7 @@ def cpu_baseline(host_layers):
         oracle.attention(layer.q, layer.k, layer.v, bias, scale=layer.scale, cap=layer.cap)
     dt = time.perf_counter() - t0
     L0 = host_layers[0]
-    fl = attn_flops(L0.B, L0.S) * len(host_layers)
+    fl = attn_flops(L0.B, L0.S, Dv=L0.v.shape[-1]) * len(host_layers)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"{len(host_layers)} of the 9 layers (projection + all {L0.S} positions x "
@@ -105,6 +106,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=3,
                     help="layers in the oracle's timed sample (about 4-5 s each on 16 cores)")
+    ap.add_argument("--dv", type=int, default=128, choices=(128, 192),
+                    help="value width (192 is the released checkpoint's; the headline "
+                         "workload uses 128)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 3 plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -132,13 +136,13 @@ def main():
     t0 = time.perf_counter()
     layers, host = [], []
     for li in range(n_layers):
-        L = workloads.make_layer("full", layer=li)
+        L = workloads.make_layer("full", layer=li, Dv=args.dv)
         if li < max(1, args.cpu_layers):
             host.append(L)
         t = {n: to_gpu(getattr(L, n)) for n in ("q", "k", "v", "pair", "weight")}
         P = L.S // 16
         t["bias"] = torch.empty((8, P, P), dtype=torch.float32, device=dev)
-        t["out"] = torch.empty_like(t["q"])
+        t["out"] = torch.empty(tuple(t["q"].shape[:3]) + (args.dv,), dtype=t["q"].dtype, device=dev)
         layers.append(t)
     torch.cuda.synchronize()
     log(f"inputs: {n_layers} layers generated and uploaded in {time.perf_counter() - t0:.1f} s")
@@ -188,10 +192,10 @@ def main():
     attn_avg = float(np.mean(attn_ms))
     proj_avg = float(np.mean(proj_ms))
 
-    fl_layer = attn_flops(1, S)
+    fl_layer = attn_flops(1, S, Dv=args.dv)
     value = n_layers * fl_layer / (ms_per_step * 1e-3) / 1e12
     achieved = fl_layer / (attn_avg * 1e-3) / 1e12
-    traffic = load_traffic(fl_layer)
+    traffic = load_traffic(fl_layer) if args.dv == 128 else None
     pb = proj_bytes(P, 128)
     log(f"step {ms_per_step:.3f} ms; attention avg {attn_avg * 1e3:.1f} us "
         f"(median {np.median(attn_ms) * 1e3:.1f}, p95 {np.percentile(attn_ms, 95) * 1e3:.1f}) "
@@ -217,7 +221,9 @@ def main():
         log(f"cpu baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
     rec = {
-        "metric": "biased-MQA fwd TFLOP/s at S=8192, H=8, d=128 bf16; % MFMA peak",
+        "metric": ("biased-MQA fwd TFLOP/s at S=8192, H=8, d=128 bf16; % MFMA peak"
+                   if args.dv == 128 else
+                   f"biased-MQA fwd TFLOP/s at S=8192, H=8, dk=128, dv={args.dv} bf16; % MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -231,7 +237,7 @@ def main():
         "data": "synthetic (seeded N(0,1)/sqrt(128) q,k,v; N(0,1) pair rep; W var 1/128)",
         "config": {"workload": "full-context: 9 independent layers, each pair-bias projection "
                                "+ biased soft-capped MQA fwd",
-                   "B": 1, "S": S, "P": P, "q_heads": 8, "kv_heads": 1, "d": 128,
+                   "B": 1, "S": S, "P": P, "q_heads": 8, "kv_heads": 1, "d": 128, "dv": args.dv,
                    "pair_channels": 128, "layers": n_layers, "softcap": cap,
                    "global_batch": 1, "seq_len": S, "parallelism": "none (1 GPU)"},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

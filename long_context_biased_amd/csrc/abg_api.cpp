@@ -114,10 +114,13 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
     return fail(ABG_ERR_UNSUPPORTED, "S = %lld: only whole 64-position tiles are supported", (long long)S);
   if (Hq != 8) return fail(ABG_ERR_UNSUPPORTED, "Hq = %lld: only 8 query heads are supported", (long long)Hq);
   if (Dk != 128) return fail(ABG_ERR_UNSUPPORTED, "Dk = %lld: only 128 is supported", (long long)Dk);
-  if (Dv != 128) return fail(ABG_ERR_UNSUPPORTED, "Dv = %lld: only 128 is supported", (long long)Dv);
+  if (Dv != 128 && Dv != 192)
+    return fail(ABG_ERR_UNSUPPORTED, "Dv = %lld: only 128 and 192 are supported", (long long)Dv);
   if (!std::isfinite(scale)) return fail(ABG_ERR_VALUE, "scale is not finite");
   if (!std::isfinite(softcap) || softcap < 0.f)
     return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
+  if (Dv == 192 && (dtype != ABG_BF16 || softcap == 0.f))
+    return fail(ABG_ERR_UNSUPPORTED, "Dv = 192 is implemented for bf16 inputs with softcap > 0 only");
   if (bias_group < 1 || bias_group > B)
     return fail(ABG_ERR_SHAPE, "bias_group = %lld must be in [1, B]", (long long)bias_group);
   const int64_t P = S / 16;
@@ -140,7 +143,7 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
   if (overlaps(out, out_bytes, v, B * S * Dv * E)) return fail(ABG_ERR_ALIAS, "out overlaps v");
   if (overlaps(out, out_bytes, bias, bias_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps bias");
 
-  abg::AttnLaunch a{q, k, v, bias, out, B, S, bias_batch_stride, bias_group,
+  abg::AttnLaunch a{q, k, v, bias, out, B, S, Dv, bias_batch_stride, bias_group,
                     scale, softcap, dtype};
   hipError_t e = abg::launch_biased_mqa_fwd(a, static_cast<hipStream_t>(stream));
   return device_status(e, "biased_mqa_fwd launch");

@@ -17,6 +17,7 @@ struct AttnLaunch {
   void* out;
   int64_t B;
   int64_t S;
+  int64_t Dv;                 // 128, or 192 (bf16 with the cap)
   int64_t bias_batch_stride;  // elements
   int64_t bias_group;
   float scale;

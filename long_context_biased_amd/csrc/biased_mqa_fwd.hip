@@ -391,23 +391,23 @@ __device__ __forceinline__ void sm_op(int pass, int x, SmState& st, const f32x16
 }
 
 // O / rowsum -> output dtype, staged through LDS (XOR-swizzled 16-byte
-// chunks) so the 32 positions x 8 heads x 128 block, contiguous in HBM, is
+// chunks) so the 32 positions x 8 heads x DV block, contiguous in HBM, is
 // written with coalesced 16-byte stores.  The caller has passed a barrier
 // after the last read of the tile buffers, and another between the staging
 // and the copy.
-template <typename T>
-__device__ __forceinline__ void stage_output(char* smem, const f32x16 (&O)[4], float rowsum,
+template <typename T, int DV = kD>
+__device__ __forceinline__ void stage_output(char* smem, const f32x16 (&O)[DV / 32], float rowsum,
                                              int r, int g, int h) {
   constexpr int E = sizeof(T);
-  constexpr int OUT_ROW = kHeads * kD * E;
+  constexpr int OUT_ROW = kHeads * DV * E;
   const float tot = rowsum + __shfl_xor(rowsum, 32);
   const float inv = 1.0f / tot;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int dv = db * 32 + 8 * j + 4 * g;
-      const int byte = (h * kD + dv) * E;
+      const int byte = (h * DV + dv) * E;
       const int chunk = byte >> 4, inb = byte & 15;
       char* dst = smem + r * OUT_ROW + ((chunk ^ r) * 16) + inb;
       if constexpr (E == 2) {
@@ -425,9 +425,9 @@ __device__ __forceinline__ void stage_output(char* smem, const f32x16 (&O)[4], f
     }
 }
 
-template <typename T, int NT>
+template <typename T, int NT, int DV = kD>
 __device__ __forceinline__ void copy_output(const char* smem, T* __restrict__ out_block, int tid) {
-  constexpr int OUT_ROW = kHeads * kD * sizeof(T);
+  constexpr int OUT_ROW = kHeads * DV * sizeof(T);
   char* ob = reinterpret_cast<char*>(out_block);
   constexpr int CHUNKS_PER_POS = OUT_ROW / 16;
   constexpr int TOTAL = kBlockPos * CHUNKS_PER_POS;
@@ -615,36 +615,77 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-namespace fp {
-constexpr int NBUF = 3;
-constexpr int ROW = kD * 2;            // bytes per K or V row
-constexpr int TILE = kTileKeys * ROW;  // 16 KiB
-constexpr int V0 = 0;
-constexpr int K0 = NBUF * TILE;
-constexpr int B0 = 2 * NBUF * TILE;
-constexpr int SMEM = B0 + NBUF * 256;
-static_assert(SMEM >= kBlockPos * kHeads * kD * 2, "output staging fits in the tile buffers");
-}  // namespace fp
+// LDS layout for value width DV (128 or 192).
+template <int DV>
+struct FP {
+  static constexpr int NBUF = 3;
+  static constexpr int NPV = DV / 32;               // 32-channel blocks of V
+  static constexpr int KROW = kD * 2;               // bytes per K row
+  static constexpr int KTILE = kTileKeys * KROW;    // 16 KiB
+  static constexpr int VROW = DV * 2;               // bytes per V row
+  static constexpr int VTILE = kTileKeys * VROW;    // 16 or 24 KiB
+  static constexpr int V0 = 0;
+  static constexpr int K0 = NBUF * VTILE;
+  static constexpr int B0 = K0 + NBUF * KTILE;
+  static constexpr int SMEM = B0 + NBUF * 256;
+  static_assert(SMEM >= kBlockPos * kHeads * DV * 2, "output staging fits in the tile buffers");
+};
 
-// MFMA order inside a stage: PV(db 0..2, half 0), QK(kc 0..7), PV(db 3, half
-// 0), PV(db 0..3, half 1).  The QK^T chain ends mid-stage, long before the
+// MFMA order inside a stage (NPV = DV / 32 blocks of value channels):
+// PV(db 0..2, half 0), QK(kc 0..7), PV(db 3..NPV-1, half 0), PV(db 0..NPV-1,
+// half 1) -- 8 + 2 NPV slots.  The QK^T chain ends mid-stage, long before the
 // next stage's softmax reads it, and the first three MFMAs read V only.
 __device__ __forceinline__ constexpr bool slot_is_qk(int j) { return j >= 3 && j <= 10; }
 __device__ __forceinline__ constexpr int slot_kc(int j) { return j - 3; }
-__device__ __forceinline__ constexpr int slot_db(int j) { return j < 3 ? j : (j == 11 ? 3 : j - 12); }
-__device__ __forceinline__ constexpr int slot_half(int j) { return j < 12 ? 0 : 1; }
+template <int NPV>
+__device__ __forceinline__ constexpr int slot_db(int j) {
+  return j < 3 ? j : (j < 8 + NPV ? j - 8 : j - 8 - NPV);
+}
+template <int NPV>
+__device__ __forceinline__ constexpr int slot_half(int j) { return j < 8 + NPV ? 0 : 1; }
+// The 96 softmax micro-ops of a stage spread over its slots: as evenly as
+// possible, the first slots taking one more.
+template <int NSLOT>
+__device__ __forceinline__ constexpr int sm_count(int j) {
+  return 96 / NSLOT + (j < 96 % NSLOT ? 1 : 0);
+}
+template <int NSLOT>
+__device__ __forceinline__ constexpr int sm_begin(int j) {
+  return j * (96 / NSLOT) + (j < 96 % NSLOT ? j : 96 % NSLOT);
+}
+
+// V rows in LDS are row-major as in HBM, in 32-byte slots (16 channels)
+// permuted per row.  DV = 128 (8 slots): slot u of row j sits at
+// u ^ (j & 3) ^ ((u & 1) << 2).  DV = 192 (12 slots, rows 384 bytes so row j
+// starts in bank half j & 1): slot u sits at u ^ (j & 2), which stays inside
+// each aligned group of 4 slots.  Either way the 8 (row, slot) pairs a
+// half-wave touches in one transposing read fall in distinct banks.
+template <int DV>
+__device__ __forceinline__ constexpr int v_physical_slot(int u, int j) {
+  return DV == 128 ? (u ^ (j & 3) ^ ((u & 1) << 2)) : (u ^ (j & 2));
+}
+template <int DV>
+__device__ __forceinline__ constexpr int v_logical_slot(int p, int j) {
+  if (DV == 128) {
+    const int ps = p ^ (j & 3);
+    return ps ^ ((ps & 1) << 2);
+  }
+  return p ^ (j & 2);
+}
 
 // A operand of K^T tiles: 8 dk values of key row kb*32 + r.
-template <int S>
+template <int DV, int S>
 __device__ __forceinline__ bf16x8 kfrag(const char* smem, const int (&kro)[8], int kb, int kc) {
-  return *reinterpret_cast<const bf16x8*>(smem + kro[kc] + S * fp::TILE + kb * 32 * fp::ROW);
+  using L = FP<DV>;
+  return *reinterpret_cast<const bf16x8*>(smem + kro[kc] + S * L::KTILE + kb * 32 * L::KROW);
 }
 // A operand of V^T tiles: 8 keys (16-key chunk kc2) of one value channel.
-template <int S>
-__device__ __forceinline__ bf16x8 vfrag(const char* smem, const int (&vro)[4], int db, int kc2) {
-  const char* p = smem + vro[db] + S * fp::TILE + kc2 * 16 * fp::ROW;
+template <int DV, int S>
+__device__ __forceinline__ bf16x8 vfrag(const char* smem, const int (&vro)[DV / 32], int db, int kc2) {
+  using L = FP<DV>;
+  const char* p = smem + vro[db] + S * L::VTILE + kc2 * 16 * L::VROW;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * fp::ROW));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * L::VROW));
   bf16x8 f;
   __builtin_memcpy(&f, &lo, 8);
   __builtin_memcpy(reinterpret_cast<char*>(&f) + 8, &hi, 8);
@@ -657,43 +698,47 @@ __device__ __forceinline__ bf16x8 vfrag(const char* smem, const int (&vro)[4], i
 // the MFMAs of all HPW heads.  ring[] holds A fragments three slots ahead;
 // the last three slots fetch the first three fragments of the following
 // stage (PV on half NKB of V stage NSV).
-template <int HPW, int SV, int SK, int KB, int NSV, int NKB>
-__device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8], const int (&vro)[4],
-                                       const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][4],
+template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB>
+__device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8], const int (&vro)[DV / 32],
+                                       const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][DV / 32],
                                        f32x16 (&sout)[HPW], const bf16x8 (&pin)[HPW][2],
                                        const f32x16 (&ssm)[HPW], const f32x2 (&beta)[HPW],
                                        float alpha, float den_a, float (&rowsum)[HPW],
                                        bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4]) {
+  constexpr int NPV = DV / 32;
+  constexpr int NSLOT = 8 + 2 * NPV;
   SmState sm[HPW];
   f32x16 acc[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) acc[hh] = f32x16{};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < NSLOT; ++j) {
     const int jn = j + 3;
-    if (jn < 16) {
-      ring[jn & 3] = slot_is_qk(jn) ? kfrag<SK>(smem, kro, KB, slot_kc(jn))
-                                    : vfrag<SV>(smem, vro, slot_db(jn), 2 * KB + slot_half(jn));
+    if (jn < NSLOT) {
+      ring[jn & 3] = slot_is_qk(jn) ? kfrag<DV, SK>(smem, kro, KB, slot_kc(jn))
+                                    : vfrag<DV, SV>(smem, vro, slot_db<NPV>(jn), 2 * KB + slot_half<NPV>(jn));
     } else {
-      ring[jn & 3] = vfrag<NSV>(smem, vro, slot_db(jn - 16), 2 * NKB);
+      ring[jn & 3] = vfrag<DV, NSV>(smem, vro, slot_db<NPV>(jn - NSLOT), 2 * NKB);
     }
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       if (slot_is_qk(j)) {
         mfma(acc[hh], ring[j & 3], qf[hh][slot_kc(j)]);
       } else {
-        mfma(O[hh][slot_db(j)], ring[j & 3], pin[hh][slot_half(j)]);
+        mfma(O[hh][slot_db<NPV>(j)], ring[j & 3], pin[hh][slot_half<NPV>(j)]);
       }
 #pragma unroll
-      for (int u = 0; u < 6; ++u)
-        sm_op(kSm.op[6 * j + u].pass, kSm.op[6 * j + u].idx, sm[hh], ssm[hh], beta[hh], alpha,
-              den_a, rowsum[hh]);
+      for (int u = 0; u < sm_count<NSLOT>(j); ++u)
+        sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh], ssm[hh],
+              beta[hh], alpha, den_a, rowsum[hh]);
     }
     // inside the slot: the MFMA first, then the LDS reads, then the VALU work
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6 * HPW, 0);
+    if (sm_count<NSLOT>(j) == 6) __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6 * HPW, 0);
+    else if (sm_count<NSLOT>(j) == 5) __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 5 * HPW, 0);
+    else __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 4 * HPW, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -738,35 +783,40 @@ __device__ __forceinline__ void lds_copy4(const float* addr, uint32_t lds) {
 #pragma clang diagnostic pop
 }
 
-template <int HPW>
+template <int HPW, int DV>
 struct FastCtx {
   static constexpr int NW = kHeads / HPW;   // waves per workgroup
-  static constexpr int LPW = 16 / NW;       // direct loads per wave per tile and operand
+  // direct 16-byte loads per lane per tile: K, V
+  static constexpr int LPW_K = FP<DV>::KTILE / (1024 * NW);
+  static constexpr int LPW_V = FP<DV>::VTILE / (1024 * NW);
+  static_assert(LPW_K * 1024 * NW == FP<DV>::KTILE && LPW_V * 1024 * NW == FP<DV>::VTILE,
+                "tiles split evenly over the waves");
   const char* kb_ptr;   // K of this batch item
   const char* vb_ptr;   // V of this batch item
   const float* bias_lane;  // compact-bias cell that this lane copies for tile 0
-  int goff_k[LPW], goff_v[LPW];  // per-lane source offsets of the direct loads
+  int goff_k[LPW_K], goff_v[LPW_V];  // per-lane source offsets of the direct loads
   int wave;             // wave index (uniform)
   float beta_mul;       // factor of the bias in the exp2 argument
 };
 
-// Direct HBM -> LDS copy of K and V of tile t into stage S (2 * LPW loads per
-// wave, 1 KiB each).
-template <int HPW, int S>
-__device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW>& c, int t) {
-  constexpr int LPW = FastCtx<HPW>::LPW;
-  const char* kt = c.kb_ptr + (int64_t)t * fp::TILE;
-  const char* vt = c.vb_ptr + (int64_t)t * fp::TILE;
-  const uint32_t lds0 = (uint32_t)(size_t)(lds_void*)smem + S * fp::TILE;
+// Direct HBM -> LDS copy of K and V of tile t into stage S (LPW_K + LPW_V
+// loads per lane, 1 KiB per wave each) and of the tile's bias cells.
+template <int HPW, int DV, int S>
+__device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV>& c, int t) {
+  using L = FP<DV>;
+  using Ctx = FastCtx<HPW, DV>;
+  const char* kt = c.kb_ptr + (int64_t)t * L::KTILE;
+  const char* vt = c.vb_ptr + (int64_t)t * L::VTILE;
+  const uint32_t lds = (uint32_t)(size_t)(lds_void*)smem;
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const uint32_t slot = lds0 + (uint32_t)((LPW * c.wave + j) * 1024);
-    lds_copy16(kt, c.goff_k[j], slot + fp::K0);
-    lds_copy16(vt, c.goff_v[j], slot + fp::V0);
-  }
+  for (int j = 0; j < Ctx::LPW_K; ++j)
+    lds_copy16(kt, c.goff_k[j], lds + L::K0 + S * L::KTILE + (uint32_t)((Ctx::LPW_K * c.wave + j) * 1024));
+#pragma unroll
+  for (int j = 0; j < Ctx::LPW_V; ++j)
+    lds_copy16(vt, c.goff_v[j], lds + L::V0 + S * L::VTILE + (uint32_t)((Ctx::LPW_V * c.wave + j) * 1024));
   // the tile's 64 compact-bias cells (8 heads x 2 query blocks x 4 key
   // blocks), one per lane of wave 0
-  if (c.wave == 0) lds_copy4(c.bias_lane + (int64_t)t * 4, (uint32_t)(size_t)(lds_void*)smem + fp::B0 + S * 256);
+  if (c.wave == 0) lds_copy4(c.bias_lane + (int64_t)t * 4, lds + L::B0 + S * 256);
 }
 
 
@@ -786,40 +836,40 @@ __device__ __forceinline__ void read_beta(const char* smem, const int (&bias_l)[
 }
 
 // One pipelined iteration for tile t in stage C.
-template <int HPW, int C>
-__device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW>& c, int t, int last,
-                                          const int (&kro)[8], const int (&vro)[4],
+template <int HPW, int DV, int C>
+__device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV>& c, int t, int last,
+                                          const int (&kro)[8], const int (&vro)[DV / 32],
                                           const int (&bias_l)[HPW], const bf16x8 (&qf)[HPW][8],
-                                          f32x16 (&O)[HPW][4], f32x16 (&S0)[HPW],
+                                          f32x16 (&O)[HPW][DV / 32], f32x16 (&S0)[HPW],
                                           f32x16 (&S1)[HPW], bf16x8 (&P0)[HPW][2],
                                           bf16x8 (&P1)[HPW][2], float alpha,
                                           float den_a, float (&rowsum)[HPW], bf16x8 (&ring)[4]) {
   constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
   // tile t+2 into the stage that held tile t-1 (clamped past the end: the
   // copy lands in a stage nobody reads again)
-  issue_tile<HPW, NN>(smem, c, min(t + 2, last));
+  issue_tile<HPW, DV, NN>(smem, c, min(t + 2, last));
   f32x2 beta[HPW];
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
   read_beta<HPW, C>(smem, bias_l, 1, c.beta_mul, beta);
-  fstage<HPW, C, NXT, 0, C, 1>(smem, kro, vro, qf, O, S0, P0, S1, beta, alpha, den_a, rowsum, P1, ring);
+  fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, qf, O, S0, P0, S1, beta, alpha, den_a, rowsum, P1, ring);
   // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
   read_beta<HPW, NXT>(smem, bias_l, 0, c.beta_mul, beta);
-  fstage<HPW, C, NXT, 1, NXT, 0>(smem, kro, vro, qf, O, S1, P1, S0, beta, alpha, den_a, rowsum, P0, ring);
+  fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, qf, O, S1, P1, S0, beta, alpha, den_a, rowsum, P0, ring);
   tile_barrier();
 }
 
 // Last tile (stage C): PV of both halves and the softmax of its second half.
-template <int HPW, int C>
-__device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[4],
-                                          const int (&bias_l)[HPW], f32x16 (&O)[HPW][4],
+template <int HPW, int DV, int C>
+__device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[DV / 32],
+                                          const int (&bias_l)[HPW], f32x16 (&O)[HPW][DV / 32],
                                           const f32x16 (&S1)[HPW], const bf16x8 (&P0)[HPW][2],
                                           float alpha, float beta_mul, float den_a,
                                           float (&rowsum)[HPW]) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const bf16x8 a = vfrag<C>(smem, vro, db, half);
+      const bf16x8 a = vfrag<DV, C>(smem, vro, db, half);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P0[hh][half]);
     }
@@ -829,24 +879,26 @@ __device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[4],
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) softmax_capped<__bf16>(S1[hh], beta[hh], alpha, den_a, rowsum[hh], P1[hh]);
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const bf16x8 a = vfrag<C>(smem, vro, db, 2 + half);
+      const bf16x8 a = vfrag<DV, C>(smem, vro, db, 2 + half);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P1[hh][half]);
     }
 }
 
-template <int HPW>
+template <int HPW, int DV>
 __global__ __launch_bounds__(64 * (kHeads / HPW), 1)
 void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                        const __bf16* __restrict__ v, const float* __restrict__ bias,
                                        __bf16* __restrict__ out, int S, int64_t bias_batch_stride,
                                        int bias_group, float alpha, float beta_mul, float den_a) {
+  using L = FP<DV>;
+  using Ctx = FastCtx<HPW, DV>;
   constexpr int NT = 64 * (kHeads / HPW);
-  constexpr int LPW = FastCtx<HPW>::LPW;
-  __shared__ __attribute__((aligned(16))) char smem[fp::SMEM];
+  constexpr int NPV = DV / 32;
+  __shared__ __attribute__((aligned(16))) char smem[L::SMEM];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -858,9 +910,9 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   const int n = S / kTileKeys;
   const int last = n - 1;
 
-  FastCtx<HPW> c;
+  Ctx c;
   c.kb_ptr = reinterpret_cast<const char*>(k + (int64_t)b * S * kD);
-  c.vb_ptr = reinterpret_cast<const char*>(v + (int64_t)b * S * kD);
+  c.vb_ptr = reinterpret_cast<const char*>(v + (int64_t)b * S * DV);
   c.beta_mul = beta_mul;
   c.wave = __builtin_amdgcn_readfirstlane(w);
   {
@@ -870,29 +922,32 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
                   ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell;
   }
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int qs = (LPW * w + j) * 64 + lane;  // 16-byte slot of this lane in a tile
+  for (int j = 0; j < Ctx::LPW_K; ++j) {
+    const int qs = (Ctx::LPW_K * w + j) * 64 + lane;  // 16-byte slot of this lane in a K tile
     const int row = qs >> 4, pc = qs & 15;
     const int key = (row & 32) | key_perm(row & 31);
-    c.goff_k[j] = key * fp::ROW + ((pc ^ (row & 15)) * 16);
-    const int ps = (pc >> 1) ^ (row & 3);     // logical 32-byte slot held by
-    const int sl = ps ^ ((ps & 1) << 2);      // physical slot pc >> 1
-    c.goff_v[j] = row * fp::ROW + (2 * sl + (pc & 1)) * 16;
+    c.goff_k[j] = key * L::KROW + ((pc ^ (row & 15)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < Ctx::LPW_V; ++j) {
+    const int qs = (Ctx::LPW_V * w + j) * 64 + lane;  // 16-byte slot of this lane in a V tile
+    const int row = qs / (L::VROW / 16), pc = qs % (L::VROW / 16);
+    c.goff_v[j] = row * L::VROW + (2 * v_logical_slot<DV>(pc >> 1, row) + (pc & 1)) * 16;
   }
   int kro[8];
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) kro[kc] = fp::K0 + r * fp::ROW + (((2 * kc + g) ^ (r & 15)) * 16);
-  int vro[4];
+  for (int kc = 0; kc < 8; ++kc) kro[kc] = L::K0 + r * L::KROW + (((2 * kc + g) ^ (r & 15)) * 16);
+  int vro[NPV];
   {
     const int i16 = lane & 15, grp = lane >> 4;
+    const int row = 8 * (grp >> 1) + (i16 >> 2);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      vro[db] = fp::V0 + (8 * (grp >> 1) + (i16 >> 2)) * fp::ROW +
-                ((((2 * db + (grp & 1)) ^ (i16 >> 2) ^ ((grp & 1) << 2))) * 32) + 8 * (i16 & 3);
+    for (int db = 0; db < NPV; ++db)
+      vro[db] = L::V0 + row * L::VROW + v_physical_slot<DV>(2 * db + (grp & 1), row) * 32 + 8 * (i16 & 3);
   }
   int bias_l[HPW];
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) bias_l[hh] = fp::B0 + ((w * HPW + hh) * 8 + (r >> 4) * 4) * 4;
+  for (int hh = 0; hh < HPW; ++hh) bias_l[hh] = L::B0 + ((w * HPW + hh) * 8 + (r >> 4) * 4) * 4;
 
   bf16x8 qf[HPW][kD / 16];
 #pragma unroll
@@ -903,18 +958,18 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     for (int kc = 0; kc < kD / 16; ++kc) qf[hh][kc] = *reinterpret_cast<const bf16x8*>(qrow + (kc * 16 + 8 * g) * 2);
   }
 
-  f32x16 O[HPW][4];
+  f32x16 O[HPW][NPV];
   float rowsum[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     rowsum[hh] = 0.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) O[hh][db] = f32x16{};
+    for (int db = 0; db < NPV; ++db) O[hh][db] = f32x16{};
   }
 
   // ---- prologue: tiles 0 and 1 -------------------------------------------------
-  issue_tile<HPW, 0>(smem, c, 0);
-  issue_tile<HPW, 1>(smem, c, min(1, last));
+  issue_tile<HPW, DV, 0>(smem, c, 0);
+  issue_tile<HPW, DV, 1>(smem, c, min(1, last));
   tile_barrier();
 
   f32x16 S0[HPW], S1[HPW];
@@ -925,39 +980,39 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     S1[hh] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      mfma(S0[hh], kfrag<0>(smem, kro, 0, kc), qf[hh][kc]);
-      mfma(S1[hh], kfrag<0>(smem, kro, 1, kc), qf[hh][kc]);
+      mfma(S0[hh], kfrag<DV, 0>(smem, kro, 0, kc), qf[hh][kc]);
+      mfma(S1[hh], kfrag<DV, 0>(smem, kro, 1, kc), qf[hh][kc]);
     }
     softmax_capped<__bf16>(S0[hh], *reinterpret_cast<const f32x2*>(smem + bias_l[hh]) * beta_mul, alpha,
                            den_a, rowsum[hh], P0[hh]);
   }
   bf16x8 ring[4];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) ring[j] = vfrag<0>(smem, vro, j, 0);
+  for (int j = 0; j < 3; ++j) ring[j] = vfrag<DV, 0>(smem, vro, j, 0);
 
   // ---- main loop, unrolled over the three stages -------------------------------------
   int t = 0;
   while (true) {
     if (t >= last) break;
-    fast_iter<HPW, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
     if (t >= last) break;
-    fast_iter<HPW, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
     if (t >= last) break;
-    fast_iter<HPW, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
   }
   switch (last % 3) {
-    case 0: fast_tail<HPW, 0>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
-    case 1: fast_tail<HPW, 1>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
-    default: fast_tail<HPW, 2>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    case 0: fast_tail<HPW, DV, 0>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    case 1: fast_tail<HPW, DV, 1>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    default: fast_tail<HPW, DV, 2>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
   }
   __syncthreads();  // the output staging reuses the tile buffers
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) stage_output<__bf16>(smem, O[hh], rowsum[hh], r, g, w * HPW + hh);
+  for (int hh = 0; hh < HPW; ++hh) stage_output<__bf16, DV>(smem, O[hh], rowsum[hh], r, g, w * HPW + hh);
   __syncthreads();
-  copy_output<__bf16, NT>(smem, out + ((int64_t)b * S + pos0) * kHeads * kD, tid);
+  copy_output<__bf16, NT, DV>(smem, out + ((int64_t)b * S + pos0) * kHeads * DV, tid);
 }
 
 template <typename T, bool CAPPED>
@@ -976,10 +1031,17 @@ hipError_t launch_typed(const AttnLaunch& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.S / kBlockPos), (unsigned)a.B);
   if constexpr (CAPPED && sizeof(T) == 2) {
     constexpr int HPW = kFastHeadsPerWave;
-    hipLaunchKernelGGL(biased_mqa_fwd_bf16_capped_kernel<HPW>, grid, dim3(64 * (kHeads / HPW)), 0,
-                       stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), a.bias, static_cast<__bf16*>(a.out),
-                       (int)a.S, a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+    if (a.Dv == 192) {
+      hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, 192>), grid, dim3(64 * (kHeads / HPW)), 0,
+                         stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                         static_cast<const __bf16*>(a.v), a.bias, static_cast<__bf16*>(a.out),
+                         (int)a.S, a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+    } else {
+      hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, 128>), grid, dim3(64 * (kHeads / HPW)), 0,
+                         stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                         static_cast<const __bf16*>(a.v), a.bias, static_cast<__bf16*>(a.out),
+                         (int)a.S, a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+    }
   } else {
     hipLaunchKernelGGL((biased_mqa_fwd_kernel<T, CAPPED>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),

@@ -134,11 +134,12 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def make_layer(name: str, layer: int = 0, *, hot: bool = False,
-               S: Optional[int] = None) -> Layer:
+               S: Optional[int] = None, Dv: int = DV) -> Layer:
     """Inputs of layer ``layer`` of workload ``name``.
 
     ``S`` overrides the sequence length (tests use short versions of a
-    workload with the same recipe).
+    workload with the same recipe); ``Dv`` the value width (192 is the
+    released checkpoint's; the workloads are stated with 128).
     """
     shp = SHAPES[name]
     S = shp.S if S is None else S
@@ -158,11 +159,11 @@ def make_layer(name: str, layer: int = 0, *, hot: bool = False,
     # Ref items are drawn first; alt items are filled in below.
     q = np.empty((B, S, HQ, DK), f32)
     k = np.empty((B, S, 1, DK), f32)
-    v = np.empty((B, S, 1, DV), f32)
+    v = np.empty((B, S, 1, Dv), f32)
     for pi in range(n_pairs):
         q[pi * group] = normal((S, HQ, DK), qkv_std)
         k[pi * group] = normal((S, 1, DK), qkv_std)
-        v[pi * group] = normal((S, 1, DV), qkv_std)
+        v[pi * group] = normal((S, 1, Dv), qkv_std)
 
     if name == "tiny":
         # Compact bias [P,P,8] given directly = pair with C = 8, W = I_8.
@@ -185,7 +186,7 @@ def make_layer(name: str, layer: int = 0, *, hot: bool = False,
                 n = hi - lo + 1
                 q[dst, lo:hi + 1] += normal((n, HQ, DK), std)
                 k[dst, lo:hi + 1] += normal((n, 1, DK), std)
-                v[dst, lo:hi + 1] += normal((n, 1, DV), std)
+                v[dst, lo:hi + 1] += normal((n, 1, Dv), std)
 
     dt = shp.dtype
     return Layer(name=name, dtype=dt, q=_cast(q, dt), k=_cast(k, dt),

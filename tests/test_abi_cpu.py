@@ -61,7 +61,9 @@ ATTN_CASES = [
     (dict(S=0), SHAPE), (dict(S=32), SHAPE), (dict(S=262144 + 64), SHAPE),
     (dict(S=8192 + 16), UNSUP), (dict(S=100), UNSUP),
     (dict(Hq=4), UNSUP), (dict(Hq=16), UNSUP),
-    (dict(Dk=64), UNSUP), (dict(Dv=192), UNSUP),
+    # (every case here must stay invalid: the pointers are not device memory)
+    (dict(Dk=64), UNSUP), (dict(Dv=64), UNSUP), (dict(Dv=256), UNSUP),
+    (dict(Dv=192, dtype=F32), UNSUP), (dict(Dv=192, softcap=0.0), UNSUP),
     (dict(scale=float("nan")), VALUE), (dict(scale=float("inf")), VALUE),
     (dict(softcap=-1.0), VALUE), (dict(softcap=float("inf")), VALUE),
     (dict(softcap=float("nan")), VALUE),

@@ -153,6 +153,44 @@ def test_attention_stress_sampled(name):
 
 
 # ---------------------------------------------------------------------------
+# Value width 192 (the released checkpoint's V), bf16 with the cap
+# ---------------------------------------------------------------------------
+DV192 = [
+    # B, S, cap, qkv_std, bias_std, n_pairs -- 1, 2, 3, 4, 9 and 32 tiles: the
+    # last tile lands in each of the three LDS stages
+    (1, 64, 5.0, 1.0, 2.0, None),
+    (2, 128, 5.0, 0.09, 1.0, None),
+    (1, 192, 5.0, 1.0, 2.0, None),
+    (4, 256, 1.5, 1.0, 3.0, 2),
+    (1, 576, 2.0, 0.09, 1.0, None),
+    (1, 2048, 5.0, 1.0, 2.0, None),
+]
+
+
+@pytest.mark.parametrize("case", DV192, ids=lambda c: "B%d_S%d_cap%g_std%g" % (c[0], c[1], c[2], c[3]))
+def test_attention_dv192(case):
+    B, S, cap, qstd, bstd, n_pairs = case
+    L = workloads.make_custom(B=B, S=S, dtype="bf16", C=32, seed=1000 + S + B, qkv_std=qstd,
+                              bias_std=bstd, Dv=192, n_pairs=n_pairs)
+    L.cap = cap
+    _, out = _run_layer(L, "cuda")
+    assert out.shape == (B, S, 8, 192)
+    ref = oracle.attention(L.q, L.k, L.v, _oracle_bias(L), scale=L.scale, cap=cap,
+                           bias_index=L.bias_index)
+    ok, ma, rel = attention_ok(out, ref, "bf16")
+    print(f"  Dv=192 B={B} S={S}: max-abs {ma:.3g} rel-L2 {rel:.3g}", flush=True)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+@pytest.mark.parametrize("qstd", [1.0 / math.sqrt(128.0), 1.0], ids=["base", "hot"])
+def test_attention_dv192_full_sampled(qstd):
+    L = workloads.make_custom(B=1, S=8192, dtype="bf16", C=128, seed=77, qkv_std=qstd,
+                              bias_std=1.0 if qstd < 1 else 2.0, Dv=192)
+    _, out = _run_layer(L, "cuda")
+    _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=11))
+
+
+# ---------------------------------------------------------------------------
 # Properties that hold at any size
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

@@ -110,9 +110,13 @@ abg_status abg_pair_bias_project(const void* pair, const void* weight, float* bi
  *   out   [B, S, Hq, Dv]  dtype, written fully; must not overlap any input.
  *
  * Non-causal, no masks.  Limits (v1): B >= 1; S % 64 == 0 and
- * 64 <= S <= 262144; Hq == 8; Dk == 128; Dv == 128; bias_group >= 1 and
- * bias_batch_stride == 0 or >= Hq*(S/16)^2; scale finite; softcap finite and
- * >= 0.
+ * 64 <= S <= 262144; Hq == 8; Dk == 128; Dv == 128, or Dv == 192 (the
+ * released checkpoint's value width, same page, section "Why stock
+ * FlashAttention was not a drop-in replacement") for ABG_BF16 with
+ * softcap > 0; bias_group >= 1 and bias_batch_stride == 0 or
+ * >= Hq*(S/16)^2; scale finite; softcap finite and >= 0.  Any other
+ * request returns ABG_ERR_UNSUPPORTED, ABG_ERR_SHAPE or ABG_ERR_VALUE before
+ * anything is enqueued.
  */
 abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
                               const float* bias, void* out,

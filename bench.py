@@ -57,9 +57,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(per_launch_flops_unit):
-    """HBM bytes per attention launch from the committed counter summary, if
-    it was taken on the current kernel source; else None."""
+def load_counters():
+    """HBM bytes and MFMA counters per attention launch from the committed
+    rocprofv3 summary, if it was taken on the current kernel source; else
+    None."""
     try:
         kv = {}
         with open(COUNTERS_FILE) as f:
@@ -69,7 +70,9 @@ def load_traffic(per_launch_flops_unit):
                     kv[k.strip()] = v.strip()
         if kv.get("source_digest") != source_digest():
             return None
-        return float(kv["hbm_bytes_per_launch"])
+        return {"hbm_bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
+                "mfma_flops_per_launch": float(kv["mfma_flops_per_launch"]),
+                "mfma_busy_frac": float(kv["mfma_busy_frac"])}
     except (OSError, KeyError, ValueError):
         return None
 
@@ -195,7 +198,7 @@ def main():
     fl_layer = attn_flops(1, S, Dv=args.dv)
     value = n_layers * fl_layer / (ms_per_step * 1e-3) / 1e12
     achieved = fl_layer / (attn_avg * 1e-3) / 1e12
-    traffic = load_traffic(fl_layer) if args.dv == 128 else None
+    counters = load_counters() if args.dv == 128 else None
     pb = proj_bytes(P, 128)
     log(f"step {ms_per_step:.3f} ms; attention avg {attn_avg * 1e3:.1f} us "
         f"(median {np.median(attn_ms) * 1e3:.1f}, p95 {np.percentile(attn_ms, 95) * 1e3:.1f}) "
@@ -243,7 +246,9 @@ def main():
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
+                     "traffic": counters["hbm_bytes_per_launch"] if counters else None,
+                     "mfma_flops_counter": counters["mfma_flops_per_launch"] if counters else None,
+                     "mfma_busy_frac_counter": counters["mfma_busy_frac"] if counters else None,
                      "kernel": "biased_mqa_fwd_bf16_capped_kernel",
                      "avg_launch_us": round(attn_avg * 1e3, 2)},
         "projection": {"bound": "hbm", "avg_launch_us": round(proj_avg * 1e3, 2),

@@ -12,7 +12,8 @@ kernel (the attention) from HIP events on its own stream, and the CPU oracle
 timed on a bounded sample (3 of the 9 layers by default) on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--cpu-layers N]
-                    [--dv 128|192] [--copy-mib N]
+                    [--dv 128|192] [--workload full|mid|shard] [--kv-splits N|auto]
+                    [--copy-mib N]
 """
 
 from __future__ import annotations
@@ -39,9 +40,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attn_flops(B, S, H=8, Dk=128, Dv=128):
-    """QK^T + PV multiply-adds, non-causal: 2 B H S^2 (Dk + Dv)."""
-    return 2.0 * B * H * S * S * (Dk + Dv)
+def attn_flops(B, S, H=8, Dk=128, Dv=128, Sq=None):
+    """QK^T + PV multiply-adds, non-causal: 2 B H Sq S (Dk + Dv) (Sq = S unless
+    only a block of query positions is computed)."""
+    return 2.0 * B * H * (S if Sq is None else Sq) * S * (Dk + Dv)
 
 
 def proj_bytes(P, C, H=8, elem=2):
@@ -112,6 +114,14 @@ def main():
     ap.add_argument("--dv", type=int, default=128, choices=(128, 192),
                     help="value width (192 is the released checkpoint's; the headline "
                          "workload uses 128)")
+    ap.add_argument("--workload", default="full", choices=("full", "mid", "shard"),
+                    help="full: the full-context layers (the headline); mid: S=2048 layers; "
+                         "shard: one GPU's share of a full-context layer under sequence "
+                         "parallelism over 8 GPUs (1024 query positions at offset 3072, all "
+                         "8192 keys)")
+    ap.add_argument("--kv-splits", default=None,
+                    help="key ranges per attention call (an integer or 'auto'; default: 1 for "
+                         "full, auto otherwise)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 3 plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -136,16 +146,27 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    from long_context_biased_amd import auto_kv_splits, workspace_bytes
+    wl = args.workload
+    if wl != "full":
+        args.no_cpu_baseline = True
     t0 = time.perf_counter()
     layers, host = [], []
     for li in range(n_layers):
-        L = workloads.make_layer("full", layer=li, Dv=args.dv)
+        L = workloads.make_layer("mid" if wl == "mid" else "full", layer=li, Dv=args.dv)
         if li < max(1, args.cpu_layers):
             host.append(L)
         t = {n: to_gpu(getattr(L, n)) for n in ("q", "k", "v", "pair", "weight")}
         P = L.S // 16
+        q_off, Sq = (3072, 1024) if wl == "shard" else (0, L.S)
+        t["q"] = t["q"][:, q_off:q_off + Sq].contiguous()
         t["bias"] = torch.empty((8, P, P), dtype=torch.float32, device=dev)
-        t["out"] = torch.empty(tuple(t["q"].shape[:3]) + (args.dv,), dtype=t["q"].dtype, device=dev)
+        t["out"] = torch.empty((1, Sq, 8, args.dv), dtype=t["q"].dtype, device=dev)
+        ks = args.kv_splits if args.kv_splits is not None else ("1" if wl == "full" else "auto")
+        z = auto_kv_splits(1, Sq, L.S) if ks == "auto" else int(ks)
+        t["z"], t["q_off"], t["Sq"] = z, q_off, Sq
+        nws = workspace_bytes(1, Sq, 8, args.dv, z)
+        t["ws"] = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev) if nws > 0 else None
         layers.append(t)
     torch.cuda.synchronize()
     log(f"inputs: {n_layers} layers generated and uploaded in {time.perf_counter() - t0:.1f} s")
@@ -165,7 +186,8 @@ def main():
             if events is not None:
                 events[li][1].record(stream)
             biased_mqa_fwd(t["q"], t["k"], t["v"], t["bias"], out=t["out"], scale=scale,
-                           softcap=cap)
+                           softcap=cap, q_offset=t["q_off"], kv_splits=t["z"],
+                           workspace=t["ws"])
             if events is not None:
                 events[li][2].record(stream)
 
@@ -195,10 +217,11 @@ def main():
     attn_avg = float(np.mean(attn_ms))
     proj_avg = float(np.mean(proj_ms))
 
-    fl_layer = attn_flops(1, S, Dv=args.dv)
+    Sq = layers[0]["Sq"]
+    fl_layer = attn_flops(1, S, Dv=args.dv, Sq=Sq)
     value = n_layers * fl_layer / (ms_per_step * 1e-3) / 1e12
     achieved = fl_layer / (attn_avg * 1e-3) / 1e12
-    counters = load_counters() if args.dv == 128 else None
+    counters = load_counters() if (args.dv == 128 and wl == "full") else None
     pb = proj_bytes(P, 128)
     log(f"step {ms_per_step:.3f} ms; attention avg {attn_avg * 1e3:.1f} us "
         f"(median {np.median(attn_ms) * 1e3:.1f}, p95 {np.percentile(attn_ms, 95) * 1e3:.1f}) "
@@ -225,8 +248,9 @@ def main():
 
     rec = {
         "metric": ("biased-MQA fwd TFLOP/s at S=8192, H=8, d=128 bf16; % MFMA peak"
-                   if args.dv == 128 else
-                   f"biased-MQA fwd TFLOP/s at S=8192, H=8, dk=128, dv={args.dv} bf16; % MFMA peak"),
+                   if (args.dv == 128 and wl == "full") else
+                   f"biased-MQA fwd TFLOP/s at S={S}, Sq={Sq}, H=8, dk=128, dv={args.dv} bf16; "
+                   f"% MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -238,9 +262,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)/sqrt(128) q,k,v; N(0,1) pair rep; W var 1/128)",
-        "config": {"workload": "full-context: 9 independent layers, each pair-bias projection "
-                               "+ biased soft-capped MQA fwd",
-                   "B": 1, "S": S, "P": P, "q_heads": 8, "kv_heads": 1, "d": 128, "dv": args.dv,
+        "config": {"workload": {"full": "full-context: 9 independent layers, each pair-bias "
+                                        "projection + biased soft-capped MQA fwd",
+                                "mid": "mid: independent S=2048 layers, each pair-bias projection "
+                                       "+ biased soft-capped MQA fwd",
+                                "shard": "one GPU's share of full-context layers (queries "
+                                         "3072..4095 of 8192, all keys; full projection)"}[wl],
+                   "B": 1, "S": S, "Sq": Sq, "kv_splits": layers[0]["z"], "P": P, "q_heads": 8,
+                   "kv_heads": 1, "d": 128, "dv": args.dv,
                    "pair_channels": 128, "layers": n_layers, "softcap": cap,
                    "global_batch": 1, "seq_len": S, "parallelism": "none (1 GPU)"},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -125,6 +125,48 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
                               float scale, float softcap,
                               abg_dtype dtype, void* stream);
 
+/* Workspace bytes that abg_biased_mqa_fwd_ex needs for kv_splits key ranges:
+ * 0 for kv_splits == 1, else kv_splits * B * Sq * Hq * (Dv + 1) * 4 (float32
+ * partial numerators and denominators).  -1 for out-of-range arguments. */
+int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
+                                           int64_t kv_splits);
+
+/* The attention of abg_biased_mqa_fwd for a block of query positions and
+ * with the keys split over several workgroups.
+ *
+ *   q     [B, Sq, Hq, Dk]: positions q_offset .. q_offset + Sq - 1 of a
+ *         sequence of Sk positions; out [B, Sq, Hq, Dv] likewise.
+ *   k, v  [B, Sk, 1, Dk] / [B, Sk, 1, Dv]; bias compact for the whole
+ *         sequence, [Hq, Sk/16, Sk/16] per block as above.  Query i uses bias
+ *         row (q_offset + i) / 16 -- the per-position bias of the logit
+ *         equation (page "Making Full-Context AlphaGenome Fit on an RTX 3090",
+ *         section "Why stock FlashAttention was not a drop-in replacement").
+ *   kv_splits  the Sk/64 key tiles are divided into kv_splits equal ranges,
+ *         each computed by its own workgroups; their partial softmax sums
+ *         are merged afterwards (section "Online softmax, one block at a
+ *         time": with the cap the maximum is fixed, so the partial
+ *         numerators and denominators simply add).  This keeps the GPU full
+ *         when B * Sq / 32 is small (short sequences, one GPU's share of the
+ *         queries).  kv_splits > 1 needs a device workspace of
+ *         abg_biased_mqa_fwd_workspace_bytes(...) bytes, owned by the caller,
+ *         16-byte aligned, not overlapping any tensor; its contents are
+ *         scratch and are overwritten.  Calls that share a workspace must be
+ *         ordered on one stream.
+ *
+ * Limits beyond abg_biased_mqa_fwd's: Sq a multiple of 32 in [32, Sk];
+ * q_offset a multiple of 16 with q_offset + Sq <= Sk; 1 <= kv_splits <= 64
+ * dividing Sk/64; kv_splits > 1 for ABG_BF16 with softcap > 0 only.
+ * abg_biased_mqa_fwd(...) equals abg_biased_mqa_fwd_ex(..., NULL, 0, B, S, S,
+ * 0, ..., 1, ...). */
+abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
+                                 const float* bias, void* out,
+                                 void* workspace, int64_t workspace_bytes,
+                                 int64_t B, int64_t Sq, int64_t Sk, int64_t q_offset,
+                                 int64_t Hq, int64_t Dk, int64_t Dv,
+                                 int64_t bias_batch_stride, int64_t bias_group,
+                                 int64_t kv_splits, float scale, float softcap,
+                                 abg_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

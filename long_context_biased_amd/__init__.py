@@ -16,9 +16,12 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     AbgError,
+    auto_kv_splits,
     biased_mqa_fwd,
     load,
     pair_bias_project,
     raw_biased_mqa_fwd,
+    raw_biased_mqa_fwd_ex,
     raw_pair_bias_project,
+    workspace_bytes,
 )

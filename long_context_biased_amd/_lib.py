@@ -24,7 +24,8 @@ STATUS = {0: "ABG_OK", 1: "ABG_ERR_NULL", 2: "ABG_ERR_SHAPE", 3: "ABG_ERR_UNSUPP
 
 #: Every symbol include/abg.h declares.
 EXPORTS = ("abg_abi_version", "abg_status_string", "abg_last_error",
-           "abg_pair_bias_project", "abg_biased_mqa_fwd")
+           "abg_pair_bias_project", "abg_biased_mqa_fwd", "abg_biased_mqa_fwd_ex",
+           "abg_biased_mqa_fwd_workspace_bytes")
 
 
 class AbgError(RuntimeError):
@@ -60,6 +61,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.abg_biased_mqa_fwd.restype = i32
     lib.abg_biased_mqa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                        i64, i64, f32, f32, i32, vp]
+    lib.abg_biased_mqa_fwd_ex.restype = i32
+    lib.abg_biased_mqa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          i64, i64, i64, i64, i64, i64, f32, f32, i32, vp]
+    lib.abg_biased_mqa_fwd_workspace_bytes.restype = i64
+    lib.abg_biased_mqa_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     _lib = lib
     return lib
 
@@ -82,6 +88,29 @@ def raw_biased_mqa_fwd(q, k, v, bias, out, B, S, Hq, Dk, Dv, bias_batch_stride,
     return load().abg_biased_mqa_fwd(q, k, v, bias, out, B, S, Hq, Dk, Dv,
                                      bias_batch_stride, bias_group, scale, softcap,
                                      dtype, stream)
+
+
+def raw_biased_mqa_fwd_ex(q, k, v, bias, out, workspace, workspace_bytes, B, Sq, Sk, q_offset,
+                          Hq, Dk, Dv, bias_batch_stride, bias_group, kv_splits, scale, softcap,
+                          dtype, stream=None) -> int:
+    return load().abg_biased_mqa_fwd_ex(q, k, v, bias, out, workspace, workspace_bytes, B, Sq,
+                                        Sk, q_offset, Hq, Dk, Dv, bias_batch_stride,
+                                        bias_group, kv_splits, scale, softcap, dtype, stream)
+
+
+def workspace_bytes(B, Sq, Hq, Dv, kv_splits) -> int:
+    """Device workspace that a call with ``kv_splits`` key ranges needs."""
+    return int(load().abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits))
+
+
+def auto_kv_splits(B, Sq, Sk, target_groups=256) -> int:
+    """Fewest key ranges (a power of two dividing the Sk/64 key tiles, at most
+    64) that give at least ``target_groups`` workgroups (one per CU)."""
+    tiles = Sk // 64
+    z = 1
+    while B * (Sq // 32) * z < target_groups and z < 64 and tiles % (2 * z) == 0:
+        z *= 2
+    return z
 
 
 # ---------------------------------------------------------------------------
@@ -139,29 +168,36 @@ def pair_bias_project(pair, weight, out=None):
 
 
 def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
-                   softcap: float = 5.0, bias_group: int = 1):
+                   softcap: float = 5.0, bias_group: int = 1, q_offset: int = 0,
+                   kv_splits=1, workspace=None):
     """Biased, soft-capped multi-query attention forward on the GPU.
 
-    ``q`` [B, S, 8, 128], ``k`` [B, S, 1, 128], ``v`` [B, S, 1, 128] (bfloat16
-    or float32); ``bias`` float32 compact bias [8, S/16, S/16] shared by all
-    items, or [Bb, 8, S/16, S/16] with item b reading block b // bias_group.
-    ``scale`` defaults to 1/sqrt(128); ``softcap`` 0 disables the cap.
-    Returns ``out`` [B, S, 8, 128] in the input dtype.
+    ``q`` [B, Sq, 8, 128] holds positions q_offset .. q_offset + Sq - 1 of a
+    sequence whose ``k`` [B, Sk, 1, 128] and ``v`` [B, Sk, 1, Dv] (bfloat16 or
+    float32; Dv 128, or 192 for bf16 with the cap) cover all Sk positions;
+    Sq == Sk and q_offset == 0 is the plain call.  ``bias`` float32 compact
+    bias [8, Sk/16, Sk/16] shared by all items, or [Bb, 8, Sk/16, Sk/16] with
+    item b reading block b // bias_group.  ``scale`` defaults to
+    1/sqrt(128); ``softcap`` 0 disables the cap.  ``kv_splits`` > 1 (or
+    "auto") computes key ranges in separate workgroups and merges them
+    (bf16 with the cap); the float32 workspace is ``workspace`` or a new
+    device tensor.  Returns ``out`` [B, Sq, 8, Dv] in the input dtype.
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (bias, "bias")):
         _dev(t, n)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, S, heads, D]")
-    B, S, Hq, Dk = q.shape
+    B, Sq, Hq, Dk = q.shape
+    Sk = k.shape[1]
     Dv = v.shape[-1]
-    if tuple(k.shape) != (B, S, 1, Dk) or tuple(v.shape[:3]) != (B, S, 1):
-        raise ValueError(f"k must be [B,S,1,Dk] and v [B,S,1,Dv]; got {tuple(k.shape)}, {tuple(v.shape)}")
+    if tuple(k.shape) != (B, Sk, 1, Dk) or tuple(v.shape[:3]) != (B, Sk, 1):
+        raise ValueError(f"k must be [B,Sk,1,Dk] and v [B,Sk,1,Dv]; got {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     if bias.dtype != torch.float32:
         raise TypeError("bias must be float32")
-    P = S // 16
+    P = Sk // 16
     if bias.dim() == 3:
         bias_stride = 0
         if tuple(bias.shape) != (Hq, P, P):
@@ -177,11 +213,27 @@ def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
     if out is None:
-        out = torch.empty((B, S, Hq, Dv), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
     _dev(out, "out")
-    if out.dtype != q.dtype or tuple(out.shape) != (B, S, Hq, Dv):
-        raise ValueError("out must match q's dtype and be [B, S, Hq, Dv]")
-    _check(raw_biased_mqa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(),
-                              out.data_ptr(), B, S, Hq, Dk, Dv, bias_stride, bias_group,
-                              float(scale), float(softcap), _dtype_code(q), _stream(q.device)))
+    if out.dtype != q.dtype or tuple(out.shape) != (B, Sq, Hq, Dv):
+        raise ValueError("out must match q's dtype and be [B, Sq, Hq, Dv]")
+    if kv_splits == "auto":
+        kv_splits = auto_kv_splits(B, Sq, Sk) if (q.dtype == torch.bfloat16 and softcap > 0) else 1
+    kv_splits = int(kv_splits)
+    if kv_splits == 1 and Sq == Sk and q_offset == 0 and workspace is None:
+        _check(raw_biased_mqa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(),
+                                  out.data_ptr(), B, Sk, Hq, Dk, Dv, bias_stride, bias_group,
+                                  float(scale), float(softcap), _dtype_code(q), _stream(q.device)))
+        return out
+    need = workspace_bytes(B, Sq, Hq, Dv, kv_splits) if kv_splits >= 1 else 0
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(raw_biased_mqa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(),
+                                 out.data_ptr(), ws_ptr, ws_bytes, B, Sq, Sk, int(q_offset), Hq,
+                                 Dk, Dv, bias_stride, bias_group, kv_splits, float(scale),
+                                 float(softcap), _dtype_code(q), _stream(q.device)))
     return out

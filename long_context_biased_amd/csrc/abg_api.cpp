@@ -99,6 +99,25 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
                               int64_t bias_batch_stride, int64_t bias_group,
                               float scale, float softcap,
                               abg_dtype dtype, void* stream) {
+  return abg_biased_mqa_fwd_ex(q, k, v, bias, out, nullptr, 0, B, S, S, 0, Hq, Dk, Dv,
+                               bias_batch_stride, bias_group, 1, scale, softcap, dtype, stream);
+}
+
+int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
+                                           int64_t kv_splits) {
+  if (B < 1 || Sq < 1 || Hq < 1 || Dv < 1 || kv_splits < 1 || kv_splits > 64) return -1;
+  if (kv_splits == 1) return 0;
+  return kv_splits * B * Sq * Hq * (Dv + 1) * 4;
+}
+
+abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
+                                 const float* bias, void* out,
+                                 void* workspace, int64_t workspace_bytes,
+                                 int64_t B, int64_t Sq, int64_t Sk, int64_t q_offset,
+                                 int64_t Hq, int64_t Dk, int64_t Dv,
+                                 int64_t bias_batch_stride, int64_t bias_group,
+                                 int64_t kv_splits, float scale, float softcap,
+                                 abg_dtype dtype, void* stream) {
   g_last_error.clear();
   if (dtype != ABG_F32 && dtype != ABG_BF16)
     return fail(ABG_ERR_VALUE, "dtype %d is not ABG_F32 or ABG_BF16", (int)dtype);
@@ -108,10 +127,20 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
   if (!bias) return fail(ABG_ERR_NULL, "bias is NULL");
   if (!out) return fail(ABG_ERR_NULL, "out is NULL");
   if (B < 1 || B > 65535) return fail(ABG_ERR_SHAPE, "B = %lld must be in [1, 65535]", (long long)B);
-  if (S < 64 || S > 262144)
-    return fail(ABG_ERR_SHAPE, "S = %lld must be in [64, 262144]", (long long)S);
-  if (S % 64 != 0)
-    return fail(ABG_ERR_UNSUPPORTED, "S = %lld: only whole 64-position tiles are supported", (long long)S);
+  if (Sk < 64 || Sk > 262144)
+    return fail(ABG_ERR_SHAPE, "S = %lld must be in [64, 262144]", (long long)Sk);
+  if (Sk % 64 != 0)
+    return fail(ABG_ERR_UNSUPPORTED, "S = %lld: only whole 64-position tiles are supported", (long long)Sk);
+  if (Sq < 32 || Sq > Sk)
+    return fail(ABG_ERR_SHAPE, "Sq = %lld must be in [32, Sk = %lld]", (long long)Sq, (long long)Sk);
+  if (Sq % 32 != 0)
+    return fail(ABG_ERR_UNSUPPORTED, "Sq = %lld: only whole 32-position query blocks are supported",
+                (long long)Sq);
+  if (q_offset < 0 || q_offset > Sk - Sq)
+    return fail(ABG_ERR_SHAPE, "q_offset = %lld must be in [0, Sk - Sq = %lld]", (long long)q_offset,
+                (long long)(Sk - Sq));
+  if (q_offset % 16 != 0)
+    return fail(ABG_ERR_UNSUPPORTED, "q_offset = %lld must be a multiple of 16", (long long)q_offset);
   if (Hq != 8) return fail(ABG_ERR_UNSUPPORTED, "Hq = %lld: only 8 query heads are supported", (long long)Hq);
   if (Dk != 128) return fail(ABG_ERR_UNSUPPORTED, "Dk = %lld: only 128 is supported", (long long)Dk);
   if (Dv != 128 && Dv != 192)
@@ -119,11 +148,24 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
   if (!std::isfinite(scale)) return fail(ABG_ERR_VALUE, "scale is not finite");
   if (!std::isfinite(softcap) || softcap < 0.f)
     return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
-  if (Dv == 192 && (dtype != ABG_BF16 || softcap == 0.f))
+  const bool fast = dtype == ABG_BF16 && softcap > 0.f;
+  if (Dv == 192 && !fast)
     return fail(ABG_ERR_UNSUPPORTED, "Dv = 192 is implemented for bf16 inputs with softcap > 0 only");
+  if (kv_splits < 1 || kv_splits > 64)
+    return fail(ABG_ERR_SHAPE, "kv_splits = %lld must be in [1, 64]", (long long)kv_splits);
+  if ((Sk / 64) % kv_splits != 0)
+    return fail(ABG_ERR_SHAPE, "kv_splits = %lld must divide the %lld key tiles", (long long)kv_splits,
+                (long long)(Sk / 64));
+  if (kv_splits > 1 && !fast)
+    return fail(ABG_ERR_UNSUPPORTED, "kv_splits > 1 is implemented for bf16 inputs with softcap > 0 only");
+  const int64_t ws_need = abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits);
+  if (kv_splits > 1 && !workspace) return fail(ABG_ERR_NULL, "workspace is NULL (kv_splits > 1)");
+  if (kv_splits > 1 && workspace_bytes < ws_need)
+    return fail(ABG_ERR_SHAPE, "workspace_bytes = %lld, need %lld", (long long)workspace_bytes,
+                (long long)ws_need);
   if (bias_group < 1 || bias_group > B)
     return fail(ABG_ERR_SHAPE, "bias_group = %lld must be in [1, B]", (long long)bias_group);
-  const int64_t P = S / 16;
+  const int64_t P = Sk / 16;
   const int64_t bias_elems = Hq * P * P;
   if (bias_batch_stride != 0 && bias_batch_stride < bias_elems)
     return fail(ABG_ERR_SHAPE, "bias_batch_stride = %lld must be 0 or >= Hq*(S/16)^2 = %lld",
@@ -132,19 +174,28 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
     return fail(ABG_ERR_ALIGN, "bias_batch_stride must be a multiple of 4 elements");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(out))
     return fail(ABG_ERR_ALIGN, "q, k, v, bias and out must be 16-byte aligned");
+  if (kv_splits > 1 && !aligned16(workspace))
+    return fail(ABG_ERR_ALIGN, "workspace must be 16-byte aligned");
   const int64_t E = elem_bytes(dtype);
-  const int64_t q_bytes = B * S * Hq * Dk * E;
-  const int64_t kv_bytes = B * S * Dk * E;
+  const int64_t q_bytes = B * Sq * Hq * Dk * E;
+  const int64_t kv_bytes = B * Sk * Dk * E;
   const int64_t n_bias = (B - 1) / bias_group + 1;
   const int64_t bias_bytes = ((n_bias - 1) * bias_batch_stride + bias_elems) * 4;
-  const int64_t out_bytes = B * S * Hq * Dv * E;
+  const int64_t out_bytes = B * Sq * Hq * Dv * E;
   if (overlaps(out, out_bytes, q, q_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps q");
   if (overlaps(out, out_bytes, k, kv_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps k");
-  if (overlaps(out, out_bytes, v, B * S * Dv * E)) return fail(ABG_ERR_ALIAS, "out overlaps v");
+  if (overlaps(out, out_bytes, v, B * Sk * Dv * E)) return fail(ABG_ERR_ALIAS, "out overlaps v");
   if (overlaps(out, out_bytes, bias, bias_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps bias");
+  if (kv_splits > 1) {
+    const void* ins[5] = {q, k, v, bias, out};
+    const int64_t sz[5] = {q_bytes, kv_bytes, B * Sk * Dv * E, bias_bytes, out_bytes};
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(workspace, ws_need, ins[i], sz[i]))
+        return fail(ABG_ERR_ALIAS, "workspace overlaps an input or the output");
+  }
 
-  abg::AttnLaunch a{q, k, v, bias, out, B, S, Dv, bias_batch_stride, bias_group,
-                    scale, softcap, dtype};
+  abg::AttnLaunch a{q, k, v, bias, out, static_cast<float*>(workspace), B, Sq, Sk, q_offset, Dv,
+                    bias_batch_stride, bias_group, kv_splits, scale, softcap, dtype};
   hipError_t e = abg::launch_biased_mqa_fwd(a, static_cast<hipStream_t>(stream));
   return device_status(e, "biased_mqa_fwd launch");
 }

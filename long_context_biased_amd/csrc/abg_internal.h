@@ -15,11 +15,15 @@ struct AttnLaunch {
   const void* v;
   const float* bias;
   void* out;
+  float* ws;                  // fp32 partials when kv_splits > 1, else unused
   int64_t B;
-  int64_t S;
+  int64_t Sq;                 // query positions in q / out
+  int64_t Sk;                 // key positions (the sequence length)
+  int64_t q_offset;           // position of q's first row in the sequence
   int64_t Dv;                 // 128, or 192 (bf16 with the cap)
   int64_t bias_batch_stride;  // elements
   int64_t bias_group;
+  int64_t kv_splits;          // key ranges computed by separate workgroups
   float scale;
   float softcap;
   abg_dtype dtype;

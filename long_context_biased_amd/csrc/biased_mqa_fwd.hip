@@ -444,8 +444,9 @@ template <typename T, bool CAPPED>
 __global__ __launch_bounds__(kThreads, 1)
 void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
                            const T* __restrict__ v, const float* __restrict__ bias,
-                           T* __restrict__ out, int S, int64_t bias_batch_stride,
-                           int bias_group, float alpha, float beta_mul, float den_a) {
+                           T* __restrict__ out, int Sq, int S, int q_offset,
+                           int64_t bias_batch_stride, int bias_group, float alpha,
+                           float beta_mul, float den_a) {
   using L = Lay<T>;
   using F = typename Traits<T>::F;
   constexpr int E = L::E;
@@ -458,7 +459,8 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int r = lane & 31;
   const int g = lane >> 5;
   const int b = blockIdx.y;
-  const int pos0 = blockIdx.x * kBlockPos;
+  const int qpos0 = blockIdx.x * kBlockPos;  // first row of this block in q / out
+  const int pos0 = q_offset + qpos0;         // its position in the sequence
   const int P = S >> 4;
   const int n = S / kTileKeys;
 
@@ -469,7 +471,7 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // ---- Q fragments (B operand), held for the whole kernel -----------------
   F qf[kD / 16];
   {
-    const char* qrow = reinterpret_cast<const char*>(q + (((int64_t)b * S + pos0 + r) * kHeads + h) * kD);
+    const char* qrow = reinterpret_cast<const char*>(q + (((int64_t)b * Sq + qpos0 + r) * kHeads + h) * kD);
 #pragma unroll
     for (int kc = 0; kc < kD / 16; ++kc) {
       const char* p = qrow + (kc * 16 + 8 * g) * E;
@@ -587,7 +589,7 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
 
   stage_output<T>(smem, O, rowsum, r, g, h);
   __syncthreads();
-  copy_output<T, kThreads>(smem, out + ((int64_t)b * S + pos0) * kHeads * kD, tid);
+  copy_output<T, kThreads>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * kD, tid);
 }
 
 // ===========================================================================
@@ -888,12 +890,17 @@ __device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[DV 
     }
 }
 
-template <int HPW, int DV>
+// Grid (Sq / 32, B, kv_splits).  With SPLIT, workgroup z covers key tiles
+// [z n, (z + 1) n) and writes its unnormalised numerator and denominator to
+// the workspace instead of the output (merged by merge_partials_kernel).
+template <int HPW, int DV, bool SPLIT>
 __global__ __launch_bounds__(64 * (kHeads / HPW), 1)
 void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                        const __bf16* __restrict__ v, const float* __restrict__ bias,
-                                       __bf16* __restrict__ out, int S, int64_t bias_batch_stride,
-                                       int bias_group, float alpha, float beta_mul, float den_a) {
+                                       __bf16* __restrict__ out, float* __restrict__ ws, int Sq,
+                                       int S, int q_offset, int tiles_per_split,
+                                       int64_t bias_batch_stride, int bias_group, float alpha,
+                                       float beta_mul, float den_a) {
   using L = FP<DV>;
   using Ctx = FastCtx<HPW, DV>;
   constexpr int NT = 64 * (kHeads / HPW);
@@ -905,21 +912,24 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   const int r = lane & 31;
   const int g = lane >> 5;
   const int b = blockIdx.y;
-  const int pos0 = blockIdx.x * kBlockPos;
+  const int split = blockIdx.z;
+  const int qpos0 = blockIdx.x * kBlockPos;  // first row of this block in q / out
+  const int pos0 = q_offset + qpos0;         // its position in the sequence
   const int P = S >> 4;
-  const int n = S / kTileKeys;
+  const int n = tiles_per_split;
   const int last = n - 1;
+  const int64_t key0 = (int64_t)split * tiles_per_split * kTileKeys;  // first key of the range
 
   Ctx c;
-  c.kb_ptr = reinterpret_cast<const char*>(k + (int64_t)b * S * kD);
-  c.vb_ptr = reinterpret_cast<const char*>(v + (int64_t)b * S * DV);
+  c.kb_ptr = reinterpret_cast<const char*>(k + ((int64_t)b * S + key0) * kD);
+  c.vb_ptr = reinterpret_cast<const char*>(v + ((int64_t)b * S + key0) * DV);
   c.beta_mul = beta_mul;
   c.wave = __builtin_amdgcn_readfirstlane(w);
   {
     // bias cell of lane l: head l>>3, query block (l>>2)&1, key block l&3
     const int bh = lane >> 3, pb = (lane >> 2) & 1, cell = lane & 3;
     c.bias_lane = bias + (int64_t)(b / bias_group) * bias_batch_stride +
-                  ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell;
+                  ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell + (key0 >> 4);
   }
 #pragma unroll
   for (int j = 0; j < Ctx::LPW_K; ++j) {
@@ -953,7 +963,7 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const char* qrow = reinterpret_cast<const char*>(
-        q + (((int64_t)b * S + pos0 + r) * kHeads + w * HPW + hh) * kD);
+        q + (((int64_t)b * Sq + qpos0 + r) * kHeads + w * HPW + hh) * kD);
 #pragma unroll
     for (int kc = 0; kc < kD / 16; ++kc) qf[hh][kc] = *reinterpret_cast<const bf16x8*>(qrow + (kc * 16 + 8 * g) * 2);
   }
@@ -1008,11 +1018,93 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     case 1: fast_tail<HPW, DV, 1>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
     default: fast_tail<HPW, DV, 2>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
   }
-  __syncthreads();  // the output staging reuses the tile buffers
+  if constexpr (SPLIT) {
+    // partial numerator rows [split][b][pos][h][DV] and denominators
+    // [split][b][pos][h], float32; lane (r, g) holds channels
+    // 32 db + 8 j + 4 g .. + 3 of its row (32 x 32 accumulator layout)
+    const int64_t rows = (int64_t)gridDim.y * Sq * kHeads;
+    float* wn = ws + ((int64_t)split * gridDim.y + b) * Sq * kHeads * DV;
+    float* wd = ws + (int64_t)gridDim.z * rows * DV + ((int64_t)split * gridDim.y + b) * Sq * kHeads;
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) stage_output<__bf16, DV>(smem, O[hh], rowsum[hh], r, g, w * HPW + hh);
-  __syncthreads();
-  copy_output<__bf16, NT, DV>(smem, out + ((int64_t)b * S + pos0) * kHeads * DV, tid);
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = w * HPW + hh;
+      const float tot = rowsum[hh] + __shfl_xor(rowsum[hh], 32);
+      float* nrow = wn + ((int64_t)(qpos0 + r) * kHeads + h) * DV + 4 * g;
+#pragma unroll
+      for (int db = 0; db < NPV; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 x = {O[hh][db][4 * j], O[hh][db][4 * j + 1], O[hh][db][4 * j + 2], O[hh][db][4 * j + 3]};
+          *reinterpret_cast<f32x4*>(nrow + 32 * db + 8 * j) = x;
+        }
+      if (g == 0) wd[(int64_t)(qpos0 + r) * kHeads + h] = tot;
+    }
+  } else {
+    __syncthreads();  // the output staging reuses the tile buffers
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) stage_output<__bf16, DV>(smem, O[hh], rowsum[hh], r, g, w * HPW + hh);
+    __syncthreads();
+    copy_output<__bf16, NT, DV>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * DV, tid);
+  }
+}
+
+// out[b, i, h, :] = sum_z n[z, b, i, h, :] / sum_z d[z, b, i, h] (bf16): the
+// merge of key ranges computed with the same fixed maximum, which adds.  One
+// thread per 4 channels; HBM-bound.
+template <int DV>
+__global__ __launch_bounds__(256)
+void merge_partials_kernel(const float* __restrict__ ws, __bf16* __restrict__ out, int64_t rows,
+                           int splits) {
+  constexpr int Q = DV / 4;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows * Q) return;
+  const int64_t row = id / Q;
+  const int c4 = (int)(id - row * Q);
+  const float* wd = ws + (int64_t)splits * rows * DV;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int z = 0; z < splits; ++z) {
+    num += *reinterpret_cast<const f32x4*>(ws + ((int64_t)z * rows + row) * DV + 4 * c4);
+    den += wd[(int64_t)z * rows + row];
+  }
+  const float inv = 1.0f / den;
+  const f32x2 a = {num[0] * inv, num[1] * inv};
+  const f32x2 c = {num[2] * inv, num[3] * inv};
+  u32x2 wv;
+  wv.x = __builtin_bit_cast(unsigned int, __builtin_convertvector(a, bf16x2));
+  wv.y = __builtin_bit_cast(unsigned int, __builtin_convertvector(c, bf16x2));
+  *reinterpret_cast<u32x2*>(out + row * DV + 4 * c4) = wv;
+}
+
+template <int DV>
+hipError_t launch_fast(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
+                       float den_a) {
+  constexpr int HPW = kFastHeadsPerWave;
+  const int splits = (int)a.kv_splits;
+  const int tiles = (int)(a.Sk / kTileKeys) / splits;
+  dim3 grid((unsigned)(a.Sq / kBlockPos), (unsigned)a.B, (unsigned)splits);
+  const __bf16* q = static_cast<const __bf16*>(a.q);
+  const __bf16* k = static_cast<const __bf16*>(a.k);
+  const __bf16* v = static_cast<const __bf16*>(a.v);
+  __bf16* out = static_cast<__bf16*>(a.out);
+  if (splits == 1) {
+    hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, false>), grid,
+                       dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, out, nullptr,
+                       (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
+                       (int)a.bias_group, alpha, beta_mul, den_a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, true>), grid,
+                     dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, out, a.ws,
+                     (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
+                     (int)a.bias_group, alpha, beta_mul, den_a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = a.B * a.Sq * kHeads;
+  const int64_t threads = rows * (DV / 4);
+  hipLaunchKernelGGL(merge_partials_kernel<DV>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, a.ws, out, rows, splits);
+  return hipGetLastError();
 }
 
 template <typename T, bool CAPPED>
@@ -1028,27 +1120,18 @@ hipError_t launch_typed(const AttnLaunch& a, hipStream_t stream) {
     alpha = a.scale * kLog2e;
     den_a = 0.f;
   }
-  dim3 grid((unsigned)(a.S / kBlockPos), (unsigned)a.B);
   if constexpr (CAPPED && sizeof(T) == 2) {
-    constexpr int HPW = kFastHeadsPerWave;
-    if (a.Dv == 192) {
-      hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, 192>), grid, dim3(64 * (kHeads / HPW)), 0,
-                         stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                         static_cast<const __bf16*>(a.v), a.bias, static_cast<__bf16*>(a.out),
-                         (int)a.S, a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
-    } else {
-      hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, 128>), grid, dim3(64 * (kHeads / HPW)), 0,
-                         stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                         static_cast<const __bf16*>(a.v), a.bias, static_cast<__bf16*>(a.out),
-                         (int)a.S, a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
-    }
+    return a.Dv == 192 ? launch_fast<192>(a, stream, alpha, beta_mul, den_a)
+                       : launch_fast<128>(a, stream, alpha, beta_mul, den_a);
   } else {
+    dim3 grid((unsigned)(a.Sq / kBlockPos), (unsigned)a.B);
     hipLaunchKernelGGL((biased_mqa_fwd_kernel<T, CAPPED>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.bias, static_cast<T*>(a.out), (int)a.S,
-                       a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+                       static_cast<const T*>(a.v), a.bias, static_cast<T*>(a.out), (int)a.Sq,
+                       (int)a.Sk, (int)a.q_offset, a.bias_batch_stride, (int)a.bias_group, alpha,
+                       beta_mul, den_a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -19,13 +19,13 @@ OK, NULL, SHAPE, UNSUP, ALIGN, VALUE, ALIAS, DEVICE = range(8)
 
 # Fake, distinct, 16-byte aligned "device" addresses: validation never
 # dereferences them, and every call below fails validation.
-Q, K, V, BIAS, OUT = (0x100000000 * (i + 1) for i in range(5))
+Q, K, V, BIAS, OUT, WS = (0x100000000 * (i + 1) for i in range(6))
 BF16, F32 = abg.ABG_BF16, abg.ABG_F32
 
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:abg_status|int|const char\*)\s+(abg_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:abg_status|int64_t|int|const char\*)\s+(abg_\w+)\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -84,6 +84,50 @@ def test_attention_rejects(kw, code):
     st = attn(**kw)
     assert st == code, (st, abg.load().abg_last_error())
     assert abg.load().abg_last_error().decode()
+
+
+def attn_ex(**kw):
+    a = dict(q=Q, k=K, v=V, bias=BIAS, out=OUT, ws=WS, ws_bytes=1 << 30, B=1, Sq=1024, Sk=8192,
+             q_offset=1024, Hq=8, Dk=128, Dv=128, bias_batch_stride=0, bias_group=1,
+             kv_splits=8, scale=0.088, softcap=5.0, dtype=BF16)
+    a.update(kw)
+    return abg.raw_biased_mqa_fwd_ex(a["q"], a["k"], a["v"], a["bias"], a["out"], a["ws"],
+                                     a["ws_bytes"], a["B"], a["Sq"], a["Sk"], a["q_offset"],
+                                     a["Hq"], a["Dk"], a["Dv"], a["bias_batch_stride"],
+                                     a["bias_group"], a["kv_splits"], a["scale"], a["softcap"],
+                                     a["dtype"], None)
+
+
+# Every case must stay invalid: the pointers are not device memory.
+ATTN_EX_CASES = [
+    (dict(Sq=1000), UNSUP), (dict(Sq=16), SHAPE), (dict(Sq=8192 + 32), SHAPE),
+    (dict(q_offset=8), UNSUP), (dict(q_offset=-16), SHAPE), (dict(q_offset=8192 - 1024 + 16), SHAPE),
+    (dict(kv_splits=0), SHAPE), (dict(kv_splits=65), SHAPE), (dict(kv_splits=3), SHAPE),
+    (dict(dtype=F32), UNSUP), (dict(softcap=0.0), UNSUP),
+    (dict(ws=None), NULL), (dict(ws_bytes=1024), SHAPE), (dict(ws=WS + 8), ALIGN),
+    (dict(ws=Q), ALIAS), (dict(ws=OUT - 1024), ALIAS),
+    (dict(Sk=8192 + 16), UNSUP), (dict(Dv=192, dtype=F32, kv_splits=1), UNSUP),
+    (dict(q=None), NULL), (dict(out=Q), ALIAS),
+]
+
+
+@pytest.mark.parametrize("kw,code", ATTN_EX_CASES, ids=lambda x: str(x))
+def test_attention_ex_rejects(kw, code):
+    st = attn_ex(**kw)
+    assert st == code, (st, abg.load().abg_last_error())
+    assert abg.load().abg_last_error().decode()
+
+
+def test_workspace_bytes():
+    assert abg.workspace_bytes(1, 2048, 8, 128, 1) == 0
+    assert abg.workspace_bytes(2, 1024, 8, 128, 4) == 4 * 2 * 1024 * 8 * 129 * 4
+    assert abg.workspace_bytes(1, 1024, 8, 192, 8) == 8 * 1024 * 8 * 193 * 4
+    for bad in [(0, 1024, 8, 128, 2), (1, 1024, 8, 128, 0), (1, 1024, 8, 128, 65)]:
+        assert abg.workspace_bytes(*bad) == -1
+    assert abg.auto_kv_splits(1, 2048, 2048) == 4
+    assert abg.auto_kv_splits(1, 8192, 8192) == 1
+    assert abg.auto_kv_splits(1, 1024, 8192) == 8
+    assert abg.auto_kv_splits(1, 64, 64) == 1
 
 
 def proj(**kw):

@@ -16,6 +16,7 @@ import torch
 import oracle
 from gpu_util import sample_rows, to_gpu, to_host, upload
 from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, workloads
+from long_context_biased_amd import workspace_bytes as abg_workspace_bytes
 from parity import attention_ok, projection_ok
 
 pytestmark = pytest.mark.gpu
@@ -188,6 +189,101 @@ def test_attention_dv192_full_sampled(qstd):
                               bias_std=1.0 if qstd < 1 else 2.0, Dv=192)
     _, out = _run_layer(L, "cuda")
     _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=11))
+
+
+# ---------------------------------------------------------------------------
+# Key ranges in separate workgroups (kv_splits) and query blocks (q_offset)
+# ---------------------------------------------------------------------------
+def _run_ex(L, q_rows, *, kv_splits, dev="cuda", workspace=None):
+    """Projection, then attention of query rows q_rows (a contiguous slice of
+    the sequence) against all keys."""
+    t = upload(L, dev)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    q = t["q"][:, q_rows.start:q_rows.stop].contiguous()
+    out = biased_mqa_fwd(q, t["k"], t["v"], bias, scale=L.scale, softcap=L.cap,
+                         bias_group=L.bias_group, q_offset=q_rows.start, kv_splits=kv_splits,
+                         workspace=workspace)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+SPLITS = [
+    # B, S, Dv, q_rows (start, stop) or None, kv_splits
+    (1, 256, 128, None, 2),
+    (2, 512, 128, None, 8),
+    (1, 2048, 128, None, 4),
+    (1, 2048, 128, None, "auto"),
+    (2, 768, 192, None, 3),
+    (1, 2048, 128, (1024, 1536), 1),
+    (1, 2048, 128, (512, 1024), 8),
+    (1, 1024, 192, (320, 832), 2),
+]
+
+
+@pytest.mark.parametrize("case", SPLITS, ids=lambda c: "B%d_S%d_dv%d_q%s_z%s" % c)
+def test_attention_splits_and_query_blocks(case):
+    B, S, Dv, qr, z = case
+    L = workloads.make_custom(B=B, S=S, dtype="bf16", C=32, seed=500 + S + B, qkv_std=1.0,
+                              bias_std=2.0, Dv=Dv)
+    rows = range(0, S) if qr is None else range(*qr)
+    out = _run_ex(L, rows, kv_splits=z)
+    bias64 = _oracle_bias(L)
+    worst = (0.0, 0.0)
+    for b in range(B):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, np.arange(rows.start, rows.stop),
+                                    scale=L.scale, cap=L.cap, bias_index=L.bias_index, batch=b)
+        ok, ma, rel = attention_ok(out[b], ref, "bf16")
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+        worst = (max(worst[0], ma), max(worst[1], rel))
+    print(f"  splits {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("dt,cap", [("f32", 5.0), ("bf16", 0.0)])
+def test_query_block_generic_kernel(dt, cap):
+    """A query block at an offset on the float32 / uncapped kernel."""
+    L = workloads.make_custom(B=2, S=1024, dtype=dt, C=16, seed=31, qkv_std=1.0, bias_std=2.0)
+    L.cap = cap
+    rows = range(384, 640)
+    out = _run_ex(L, rows, kv_splits=1)
+    bias64 = _oracle_bias(L)
+    for b in range(2):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, np.arange(384, 640), scale=L.scale,
+                                    cap=cap, batch=b)
+        ok, ma, rel = attention_ok(out[b], ref, dt)
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+def test_one_gpu_share_of_the_full_context():
+    """The shape one GPU of eight would compute under sequence parallelism:
+    1024 query positions at offset 3072 against all 8192 keys, 8 key ranges."""
+    L = workloads.make_layer("full", layer=4)
+    out = _run_ex(L, range(3072, 4096), kv_splits=8)
+    bias64 = _oracle_bias(L)
+    rows = np.array(sorted(set([0, 1, 15, 16, 31, 32, 511, 512, 1000, 1023] +
+                               list(np.random.Generator(np.random.PCG64(9)).integers(0, 1024, 12)))))
+    ref = oracle.attention_rows(L.q, L.k, L.v, bias64, 3072 + rows, scale=L.scale, cap=L.cap)
+    ok, ma, rel = attention_ok(out[0, rows], ref, "bf16")
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+def test_split_workspace_reuse():
+    """Two calls in a row through one workspace (the second smaller) each
+    equal a call with a fresh workspace; splits agree with the single-range
+    kernel to bf16 rounding."""
+    L = workloads.make_custom(B=1, S=2048, dtype="bf16", C=32, seed=3, qkv_std=1.0, bias_std=2.0)
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    ws = torch.empty(abg_workspace_bytes(1, 2048, 8, 128, 8), dtype=torch.uint8, device="cuda")
+    a = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, kv_splits=8, workspace=ws)
+    q2 = t["q"][:, :512].contiguous()
+    b2 = biased_mqa_fwd(q2, t["k"], t["v"], bias, kv_splits=4, workspace=ws)
+    a_ref = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, kv_splits=8)
+    b_ref = biased_mqa_fwd(q2, t["k"], t["v"], bias, kv_splits=4)
+    one = biased_mqa_fwd(t["q"], t["k"], t["v"], bias)
+    torch.cuda.synchronize()
+    assert torch.equal(a, a_ref) and torch.equal(b2, b_ref)
+    diff = (a.float() - one.float()).abs().max().item()
+    assert diff <= 2e-2 * max(1.0, one.float().abs().max().item()), diff
 
 
 # ---------------------------------------------------------------------------

@@ -157,7 +157,7 @@ def main():
         if li < max(1, args.cpu_layers):
             host.append(L)
         t = {n: to_gpu(getattr(L, n)) for n in ("q", "k", "v", "pair", "weight")}
-        P = L.S // 16
+        P = -(-L.S // 16)
         q_off, Sq = (3072, 1024) if wl == "shard" else (0, L.S)
         t["q"] = t["q"][:, q_off:q_off + Sq].contiguous()
         t["bias"] = torch.empty((8, P, P), dtype=torch.float32, device=dev)
@@ -172,7 +172,7 @@ def main():
     log(f"inputs: {n_layers} layers generated and uploaded in {time.perf_counter() - t0:.1f} s")
     host0 = host[0]
     S = host0.S
-    P = S // 16
+    P = -(-S // 16)
     scale = host0.scale
     cap = host0.cap
 

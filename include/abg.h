@@ -102,21 +102,24 @@ abg_status abg_pair_bias_project(const void* pair, const void* weight, float* bi
  *   q     [B, S, Hq, Dk]  dtype
  *   k     [B, S, 1, Dk]   dtype   (one K head shared by all query heads)
  *   v     [B, S, 1, Dv]   dtype   (one V head shared by all query heads)
- *   bias  float32 compact bias; batch item b reads the [Hq, S/16, S/16]
- *         block at  bias + (b / bias_group) * bias_batch_stride  (elements).
+ *   bias  float32 compact bias; batch item b reads the [Hq, P, P] block
+ *         (P = ceil(S/16): a last cell of fewer than 16 positions still has
+ *         its row and column) at  bias + (b / bias_group) * bias_batch_stride
+ *         (elements).
  *         bias_batch_stride = 0 shares one bias by every item; bias_group is
  *         the number of consecutive items that share a block (e.g. 2 for a
  *         REF/ALT pair).
  *   out   [B, S, Hq, Dv]  dtype, written fully; must not overlap any input.
  *
- * Non-causal, no masks.  Limits (v1): B >= 1; S % 64 == 0 and
- * 64 <= S <= 262144; Hq == 8; Dk == 128; Dv == 128, or Dv == 192 (the
- * released checkpoint's value width, same page, section "Why stock
- * FlashAttention was not a drop-in replacement") for ABG_BF16 with
- * softcap > 0; bias_group >= 1 and bias_batch_stride == 0 or
- * >= Hq*(S/16)^2; scale finite; softcap finite and >= 0.  Any other
- * request returns ABG_ERR_UNSUPPORTED, ABG_ERR_SHAPE or ABG_ERR_VALUE before
- * anything is enqueued.
+ * Non-causal, no masks.  Limits (v1): B >= 1; 1 <= S <= 262144, and
+ * S % 64 == 0 unless dtype is ABG_BF16 with softcap > 0 (that path takes
+ * any length); Hq == 8; Dk == 128; Dv == 128, or Dv == 192 (the released
+ * checkpoint's value width, same page, section "Why stock FlashAttention
+ * was not a drop-in replacement") for ABG_BF16 with softcap > 0;
+ * bias_group >= 1 and bias_batch_stride == 0 or >= Hq*P^2 (a multiple of
+ * 4); scale finite; softcap finite and >= 0.  Any other request returns
+ * ABG_ERR_UNSUPPORTED, ABG_ERR_SHAPE or ABG_ERR_VALUE before anything is
+ * enqueued.
  */
 abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
                               const float* bias, void* out,
@@ -137,11 +140,11 @@ int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, in
  *   q     [B, Sq, Hq, Dk]: positions q_offset .. q_offset + Sq - 1 of a
  *         sequence of Sk positions; out [B, Sq, Hq, Dv] likewise.
  *   k, v  [B, Sk, 1, Dk] / [B, Sk, 1, Dv]; bias compact for the whole
- *         sequence, [Hq, Sk/16, Sk/16] per block as above.  Query i uses bias
+ *         sequence, [Hq, P, P] per block as above (P = ceil(Sk/16)).  Query i uses bias
  *         row (q_offset + i) / 16 -- the per-position bias of the logit
  *         equation (page "Making Full-Context AlphaGenome Fit on an RTX 3090",
  *         section "Why stock FlashAttention was not a drop-in replacement").
- *   kv_splits  the Sk/64 key tiles are divided into kv_splits equal ranges,
+ *   kv_splits  the ceil(Sk/64) key tiles are divided into kv_splits equal ranges,
  *         each computed by its own workgroups; their partial softmax sums
  *         are merged afterwards (section "Online softmax, one block at a
  *         time": with the cap the maximum is fixed, so the partial
@@ -153,9 +156,10 @@ int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, in
  *         scratch and are overwritten.  Calls that share a workspace must be
  *         ordered on one stream.
  *
- * Limits beyond abg_biased_mqa_fwd's: Sq a multiple of 32 in [32, Sk];
- * q_offset a multiple of 16 with q_offset + Sq <= Sk; 1 <= kv_splits <= 64
- * dividing Sk/64; kv_splits > 1 for ABG_BF16 with softcap > 0 only.
+ * Limits beyond abg_biased_mqa_fwd's: 1 <= Sq <= Sk, Sq a multiple of 32
+ * unless dtype is ABG_BF16 with softcap > 0; q_offset a multiple of 16 with
+ * q_offset + Sq <= Sk; 1 <= kv_splits <= 64 dividing ceil(Sk/64);
+ * kv_splits > 1 for ABG_BF16 with softcap > 0 only.
  * abg_biased_mqa_fwd(...) equals abg_biased_mqa_fwd_ex(..., NULL, 0, B, S, S,
  * 0, ..., 1, ...). */
 abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,

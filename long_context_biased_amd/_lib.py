@@ -104,11 +104,12 @@ def workspace_bytes(B, Sq, Hq, Dv, kv_splits) -> int:
 
 
 def auto_kv_splits(B, Sq, Sk, target_groups=256) -> int:
-    """Fewest key ranges (a power of two dividing the Sk/64 key tiles, at most
-    64) that give at least ``target_groups`` workgroups (one per CU)."""
-    tiles = Sk // 64
+    """Fewest key ranges (a power of two dividing the ceil(Sk/64) key tiles,
+    at most 64) that give at least ``target_groups`` workgroups (one per CU)."""
+    tiles = -(-Sk // 64)
+    blocks = -(-Sq // 32)
     z = 1
-    while B * (Sq // 32) * z < target_groups and z < 64 and tiles % (2 * z) == 0:
+    while B * blocks * z < target_groups and z < 64 and tiles % (2 * z) == 0:
         z *= 2
     return z
 
@@ -197,7 +198,7 @@ def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
         raise TypeError("q, k, v must share a dtype")
     if bias.dtype != torch.float32:
         raise TypeError("bias must be float32")
-    P = Sk // 16
+    P = (Sk + 15) // 16  # compact bias cells per side
     if bias.dim() == 3:
         bias_stride = 0
         if tuple(bias.shape) != (Hq, P, P):

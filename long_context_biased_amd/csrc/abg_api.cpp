@@ -127,15 +127,22 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
   if (!bias) return fail(ABG_ERR_NULL, "bias is NULL");
   if (!out) return fail(ABG_ERR_NULL, "out is NULL");
   if (B < 1 || B > 65535) return fail(ABG_ERR_SHAPE, "B = %lld must be in [1, 65535]", (long long)B);
-  if (Sk < 64 || Sk > 262144)
-    return fail(ABG_ERR_SHAPE, "S = %lld must be in [64, 262144]", (long long)Sk);
-  if (Sk % 64 != 0)
-    return fail(ABG_ERR_UNSUPPORTED, "S = %lld: only whole 64-position tiles are supported", (long long)Sk);
-  if (Sq < 32 || Sq > Sk)
-    return fail(ABG_ERR_SHAPE, "Sq = %lld must be in [32, Sk = %lld]", (long long)Sq, (long long)Sk);
-  if (Sq % 32 != 0)
-    return fail(ABG_ERR_UNSUPPORTED, "Sq = %lld: only whole 32-position query blocks are supported",
-                (long long)Sq);
+  if (!std::isfinite(softcap) || softcap < 0.f)
+    return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
+  // the bf16 path with the cap takes any length; the others whole tiles
+  const bool fast = dtype == ABG_BF16 && softcap > 0.f;
+  if (Sk < 1 || Sk > 262144)
+    return fail(ABG_ERR_SHAPE, "S = %lld must be in [1, 262144]", (long long)Sk);
+  if (!fast && Sk % 64 != 0)
+    return fail(ABG_ERR_UNSUPPORTED,
+                "S = %lld: lengths that are not a multiple of 64 are implemented for bf16 inputs with "
+                "softcap > 0 only", (long long)Sk);
+  if (Sq < 1 || Sq > Sk)
+    return fail(ABG_ERR_SHAPE, "Sq = %lld must be in [1, Sk = %lld]", (long long)Sq, (long long)Sk);
+  if (!fast && Sq % 32 != 0)
+    return fail(ABG_ERR_UNSUPPORTED,
+                "Sq = %lld: query counts that are not a multiple of 32 are implemented for bf16 inputs "
+                "with softcap > 0 only", (long long)Sq);
   if (q_offset < 0 || q_offset > Sk - Sq)
     return fail(ABG_ERR_SHAPE, "q_offset = %lld must be in [0, Sk - Sq = %lld]", (long long)q_offset,
                 (long long)(Sk - Sq));
@@ -146,16 +153,14 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
   if (Dv != 128 && Dv != 192)
     return fail(ABG_ERR_UNSUPPORTED, "Dv = %lld: only 128 and 192 are supported", (long long)Dv);
   if (!std::isfinite(scale)) return fail(ABG_ERR_VALUE, "scale is not finite");
-  if (!std::isfinite(softcap) || softcap < 0.f)
-    return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
-  const bool fast = dtype == ABG_BF16 && softcap > 0.f;
   if (Dv == 192 && !fast)
     return fail(ABG_ERR_UNSUPPORTED, "Dv = 192 is implemented for bf16 inputs with softcap > 0 only");
   if (kv_splits < 1 || kv_splits > 64)
     return fail(ABG_ERR_SHAPE, "kv_splits = %lld must be in [1, 64]", (long long)kv_splits);
-  if ((Sk / 64) % kv_splits != 0)
+  const int64_t tiles = (Sk + 63) / 64;
+  if (tiles % kv_splits != 0)
     return fail(ABG_ERR_SHAPE, "kv_splits = %lld must divide the %lld key tiles", (long long)kv_splits,
-                (long long)(Sk / 64));
+                (long long)tiles);
   if (kv_splits > 1 && !fast)
     return fail(ABG_ERR_UNSUPPORTED, "kv_splits > 1 is implemented for bf16 inputs with softcap > 0 only");
   const int64_t ws_need = abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits);
@@ -165,10 +170,10 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
                 (long long)ws_need);
   if (bias_group < 1 || bias_group > B)
     return fail(ABG_ERR_SHAPE, "bias_group = %lld must be in [1, B]", (long long)bias_group);
-  const int64_t P = Sk / 16;
+  const int64_t P = (Sk + 15) / 16;  // compact bias cells per side
   const int64_t bias_elems = Hq * P * P;
   if (bias_batch_stride != 0 && bias_batch_stride < bias_elems)
-    return fail(ABG_ERR_SHAPE, "bias_batch_stride = %lld must be 0 or >= Hq*(S/16)^2 = %lld",
+    return fail(ABG_ERR_SHAPE, "bias_batch_stride = %lld must be 0 or >= Hq*ceil(S/16)^2 = %lld",
                 (long long)bias_batch_stride, (long long)bias_elems);
   if (bias_batch_stride % 4 != 0)
     return fail(ABG_ERR_ALIGN, "bias_batch_stride must be a multiple of 4 elements");

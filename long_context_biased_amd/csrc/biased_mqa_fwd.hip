@@ -243,13 +243,26 @@ __device__ __forceinline__ void pv_half(const char* buf, int vbase,
     }
 }
 
+// Keys past the end of the sequence get p = 0.  A lane (g = lane >> 5)
+// holds, for one 32-key half of a tile, 8 packed probability pairs; pair m
+// covers keys 16 (m >> 2) + 8 g + 2 (m & 3) and the next one, counted from the
+// half's first key.  `k` is that offset without the 8 g term and `lim` the
+// number of keys of the sequence from the half's first key on, less 8 g.
+// The low 16 bits of a pair hold its first key.
+__device__ __forceinline__ int lane_g() { return (int)(threadIdx.x >> 5) & 1; }
+__device__ __forceinline__ bf16x2 mask_pair(bf16x2 p, int k, int lim) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, p);
+  return __builtin_bit_cast(bf16x2, k + 1 < lim ? u : (k < lim ? (u & 0xFFFFu) : 0u));
+}
+
 // Soft-capped weights exp(L - cap) of 16 scores (key cells beta.x for x < 8,
 // beta.y for x >= 8), packed as the PV operand; the row sum adds the packed
 // values.
-template <typename T>
+template <typename T, bool MASK = false>
 __device__ __forceinline__ void softmax_capped(const f32x16& s, f32x2 beta, float alpha,
                                                float den_a, float& rowsum,
-                                               typename Traits<T>::F (&p)[2]) {
+                                               typename Traits<T>::F (&p)[2],
+                                               int lim = 0) {
   float w[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
@@ -267,6 +280,7 @@ __device__ __forceinline__ void softmax_capped(const f32x16& s, f32x2 beta, floa
       for (int m = 0; m < 4; ++m) {
         const f32x2 two = {w[8 * half + 2 * m], w[8 * half + 2 * m + 1]};
         pr[m] = __builtin_convertvector(two, bf16x2);
+        if constexpr (MASK) pr[m] = mask_pair(pr[m], 16 * half + 2 * m, lim);
         rowsum = __builtin_amdgcn_fdot2_f32_bf16(pr[m], ones, rowsum, false);
       }
       bf16x8 f;
@@ -426,7 +440,8 @@ __device__ __forceinline__ void stage_output(char* smem, const f32x16 (&O)[DV / 
 }
 
 template <typename T, int NT, int DV = kD>
-__device__ __forceinline__ void copy_output(const char* smem, T* __restrict__ out_block, int tid) {
+__device__ __forceinline__ void copy_output(const char* smem, T* __restrict__ out_block, int tid,
+                                            int valid_rows = kBlockPos) {
   constexpr int OUT_ROW = kHeads * DV * sizeof(T);
   char* ob = reinterpret_cast<char*>(out_block);
   constexpr int CHUNKS_PER_POS = OUT_ROW / 16;
@@ -435,8 +450,9 @@ __device__ __forceinline__ void copy_output(const char* smem, T* __restrict__ ou
   for (int i = 0; i < TOTAL / NT; ++i) {
     const int id = tid + NT * i;
     const int rr = id / CHUNKS_PER_POS, c = id % CHUNKS_PER_POS;
-    *reinterpret_cast<u32x4*>(ob + (int64_t)id * 16) =
-        *reinterpret_cast<const u32x4*>(smem + rr * OUT_ROW + ((c ^ rr) * 16));
+    if (rr < valid_rows)
+      *reinterpret_cast<u32x4*>(ob + (int64_t)id * 16) =
+          *reinterpret_cast<const u32x4*>(smem + rr * OUT_ROW + ((c ^ rr) * 16));
   }
 }
 
@@ -701,7 +717,8 @@ __device__ __forceinline__ bf16x8 vfrag(const char* smem, const int (&vro)[DV / 
 // the last three slots fetch the first three fragments of the following
 // stage (PV on half NKB of V stage NSV).
 template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB>
-__device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8], const int (&vro)[DV / 32],
+__device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
+                                       const int (&vro)[DV / 32],
                                        const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][DV / 32],
                                        f32x16 (&sout)[HPW], const bf16x8 (&pin)[HPW][2],
                                        const f32x16 (&ssm)[HPW], const f32x2 (&beta)[HPW],
@@ -731,8 +748,8 @@ __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8], co
       }
 #pragma unroll
       for (int u = 0; u < sm_count<NSLOT>(j); ++u)
-        sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh], ssm[hh],
-              beta[hh], alpha, den_a, rowsum[hh]);
+        sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh],
+              ssm[hh], beta[hh], alpha, den_a, rowsum[hh]);
     }
     // inside the slot: the MFMA first, then the LDS reads, then the VALU work
 #pragma unroll
@@ -797,28 +814,42 @@ struct FastCtx {
   const char* vb_ptr;   // V of this batch item
   const float* bias_lane;  // compact-bias cell that this lane copies for tile 0
   int goff_k[LPW_K], goff_v[LPW_V];  // per-lane source offsets of the direct loads
+  // A tile that ends the sequence early: its relative index in this
+  // workgroup's range (or -1) and its number of keys.  Its copies are clamped
+  // to its last row (rows past the end get finite data of that row, and p = 0
+  // from the mask), and the bias cells to the last cell: bias_cap is the
+  // largest cell offset from bias_lane that stays in the bias row.
+  int tile_end, kv_end;
+  int bias_cap;
   int wave;             // wave index (uniform)
   float beta_mul;       // factor of the bias in the exp2 argument
 };
 
 // Direct HBM -> LDS copy of K and V of tile t into stage S (LPW_K + LPW_V
 // loads per lane, 1 KiB per wave each) and of the tile's bias cells.
-template <int HPW, int DV, int S>
+template <int HPW, int DV, bool TAIL, int S>
 __device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV>& c, int t) {
   using L = FP<DV>;
   using Ctx = FastCtx<HPW, DV>;
   const char* kt = c.kb_ptr + (int64_t)t * L::KTILE;
   const char* vt = c.vb_ptr + (int64_t)t * L::VTILE;
   const uint32_t lds = (uint32_t)(size_t)(lds_void*)smem;
+  // rows of the tile that exist (uniform); the offsets of rows past them are
+  // clamped to the last 16 bytes of the last one
+  const int rows = (TAIL && t == c.tile_end) ? c.kv_end : kTileKeys;
+  const int kcap = rows * L::KROW - 16, vcap = rows * L::VROW - 16;
 #pragma unroll
   for (int j = 0; j < Ctx::LPW_K; ++j)
-    lds_copy16(kt, c.goff_k[j], lds + L::K0 + S * L::KTILE + (uint32_t)((Ctx::LPW_K * c.wave + j) * 1024));
+    lds_copy16(kt, TAIL ? min(c.goff_k[j], kcap) : c.goff_k[j],
+               lds + L::K0 + S * L::KTILE + (uint32_t)((Ctx::LPW_K * c.wave + j) * 1024));
 #pragma unroll
   for (int j = 0; j < Ctx::LPW_V; ++j)
-    lds_copy16(vt, c.goff_v[j], lds + L::V0 + S * L::VTILE + (uint32_t)((Ctx::LPW_V * c.wave + j) * 1024));
+    lds_copy16(vt, TAIL ? min(c.goff_v[j], vcap) : c.goff_v[j],
+               lds + L::V0 + S * L::VTILE + (uint32_t)((Ctx::LPW_V * c.wave + j) * 1024));
   // the tile's 64 compact-bias cells (8 heads x 2 query blocks x 4 key
   // blocks), one per lane of wave 0
-  if (c.wave == 0) lds_copy4(c.bias_lane + (int64_t)t * 4, lds + L::B0 + S * 256);
+  if (c.wave == 0)
+    lds_copy4(c.bias_lane + (TAIL ? min(4 * t, c.bias_cap) : 4 * t), lds + L::B0 + S * 256);
 }
 
 
@@ -838,7 +869,7 @@ __device__ __forceinline__ void read_beta(const char* smem, const int (&bias_l)[
 }
 
 // One pipelined iteration for tile t in stage C.
-template <int HPW, int DV, int C>
+template <int HPW, int DV, bool TAIL, int C>
 __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV>& c, int t, int last,
                                           const int (&kro)[8], const int (&vro)[DV / 32],
                                           const int (&bias_l)[HPW], const bf16x8 (&qf)[HPW][8],
@@ -849,7 +880,7 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV>& c,
   constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
   // tile t+2 into the stage that held tile t-1 (clamped past the end: the
   // copy lands in a stage nobody reads again)
-  issue_tile<HPW, DV, NN>(smem, c, min(t + 2, last));
+  issue_tile<HPW, DV, TAIL, NN>(smem, c, min(t + 2, last));
   f32x2 beta[HPW];
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
   read_beta<HPW, C>(smem, bias_l, 1, c.beta_mul, beta);
@@ -861,8 +892,8 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV>& c,
 }
 
 // Last tile (stage C): PV of both halves and the softmax of its second half.
-template <int HPW, int DV, int C>
-__device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[DV / 32],
+template <int HPW, int DV, bool TAIL, int C>
+__device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, const int (&vro)[DV / 32],
                                           const int (&bias_l)[HPW], f32x16 (&O)[HPW][DV / 32],
                                           const f32x16 (&S1)[HPW], const bf16x8 (&P0)[HPW][2],
                                           float alpha, float beta_mul, float den_a,
@@ -878,8 +909,10 @@ __device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[DV 
   f32x2 beta[HPW];
   read_beta<HPW, C>(smem, bias_l, 1, beta_mul, beta);
   bf16x8 P1[HPW][2];
+  const int lim = klim_half1 - 8 * lane_g();
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) softmax_capped<__bf16>(S1[hh], beta[hh], alpha, den_a, rowsum[hh], P1[hh]);
+  for (int hh = 0; hh < HPW; ++hh)
+    softmax_capped<__bf16, TAIL>(S1[hh], beta[hh], alpha, den_a, rowsum[hh], P1[hh], lim);
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -890,10 +923,85 @@ __device__ __forceinline__ void fast_tail(const char* smem, const int (&vro)[DV 
     }
 }
 
+// B operand of QK^T: lane (r, g) holds dk 16 kc + 8 g .. + 7 of its query
+// row, for the HPW heads that follow `qrow`.
+template <int HPW>
+__device__ __forceinline__ void load_q(const __bf16* qrow, int g, bf16x8 (&qf)[HPW][kD / 16]) {
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int kc = 0; kc < kD / 16; ++kc)
+      qf[hh][kc] = *reinterpret_cast<const bf16x8*>(qrow + hh * kD + kc * 16 + 8 * g);
+}
+// LDS offsets of the K^T A operand (key row r, XOR-swizzled 16-byte chunks).
+template <int DV>
+__device__ __forceinline__ void k_read_offsets(int r, int g, int (&kro)[8]) {
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) kro[kc] = FP<DV>::K0 + r * FP<DV>::KROW + (((2 * kc + g) ^ (r & 15)) * 16);
+}
+
+// A tile that ends the sequence early, in stage C, taken on its own after
+// the pipelined tiles: QK of both halves, the masked softmax, PV of both
+// halves.  `lim0` is the number of keys of the sequence from the tile's
+// first key on; `qb` points at the first of the wave's heads in query row
+// qpos0 of this workgroup (rows past Sq read row Sq - 1).  Q and the K
+// offsets are loaded again here rather than kept from the start: holding
+// them past the pipelined loop costs more registers than that loop leaves.
+template <int HPW, int DV, int C>
+__device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpos0, int Sq, const char* smem,
+                                             const int (&vro)[DV / 32], const int (&bias_l)[HPW],
+                                             f32x16 (&O)[HPW][DV / 32], float alpha, float beta_mul,
+                                             float den_a, float (&rowsum)[HPW]) {
+  // opaque to the compiler, so that it reloads instead of reusing the values
+  // read before the loop
+  int lane = (int)threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 5;
+  const __bf16* qrow = qb + (int64_t)(min(qpos0 + (lane & 31), Sq - 1) - qpos0) * kHeads * kD;
+  bf16x8 qf[HPW][kD / 16];
+  load_q<HPW>(qrow, g, qf);
+  int kro[8];
+  k_read_offsets<DV>(lane & 31, g, kro);
+  const int lim = lim0 - 8 * g;
+  // QK of both halves first, so that Q and the K offsets are dead before
+  // the value fragments are read
+  f32x16 sc[2][HPW];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      sc[kb][hh] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) mfma(sc[kb][hh], kfrag<DV, C>(smem, kro, kb, kc), qf[hh][kc]);
+    }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    __builtin_amdgcn_sched_barrier(0);
+    f32x2 beta[HPW];
+    read_beta<HPW, C>(smem, bias_l, kb, beta_mul, beta);
+    bf16x8 P[HPW][2];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+      softmax_capped<__bf16, true>(sc[kb][hh], beta[hh], alpha, den_a, rowsum[hh], P[hh], lim - 32 * kb);
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 a = vfrag<DV, C>(smem, vro, db, 2 * kb + half);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P[hh][half]);
+      }
+  }
+}
+
 // Grid (Sq / 32, B, kv_splits).  With SPLIT, workgroup z covers key tiles
 // [z n, (z + 1) n) and writes its unnormalised numerator and denominator to
 // the workspace instead of the output (merged by merge_partials_kernel).
-template <int HPW, int DV, bool SPLIT>
+// TAIL: S not a multiple of 64 or Sq not a multiple of 32.  The tile that
+// ends the sequence is copied with its rows past the end clamped to its last
+// row and those keys masked (p = 0); query rows past Sq read row Sq - 1 and
+// store nothing.
+template <int HPW, int DV, bool SPLIT, bool TAIL>
 __global__ __launch_bounds__(64 * (kHeads / HPW), 1)
 void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                        const __bf16* __restrict__ v, const float* __restrict__ bias,
@@ -915,10 +1023,12 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   const int split = blockIdx.z;
   const int qpos0 = blockIdx.x * kBlockPos;  // first row of this block in q / out
   const int pos0 = q_offset + qpos0;         // its position in the sequence
-  const int P = S >> 4;
+  const int P = (S + 15) >> 4;
   const int n = tiles_per_split;
   const int last = n - 1;
   const int64_t key0 = (int64_t)split * tiles_per_split * kTileKeys;  // first key of the range
+  const int klim = S - (int)key0;  // keys of the sequence from key0 on
+  const int kv_end = S - kTileKeys * ((S + kTileKeys - 1) / kTileKeys - 1);  // keys in the last tile
 
   Ctx c;
   c.kb_ptr = reinterpret_cast<const char*>(k + ((int64_t)b * S + key0) * kD);
@@ -928,8 +1038,12 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   {
     // bias cell of lane l: head l>>3, query block (l>>2)&1, key block l&3
     const int bh = lane >> 3, pb = (lane >> 2) & 1, cell = lane & 3;
-    c.bias_lane = bias + (int64_t)(b / bias_group) * bias_batch_stride +
-                  ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell + (key0 >> 4);
+    const int qrow = min((pos0 >> 4) + pb, P - 1);  // clamped: query rows past the end
+    const float* row = bias + (int64_t)(b / bias_group) * bias_batch_stride + ((int64_t)bh * P + qrow) * P;
+    c.bias_lane = row + cell + (key0 >> 4);
+    c.bias_cap = P - 1 - cell - (int)(key0 >> 4);
+    c.tile_end = (TAIL && split == (int)gridDim.z - 1 && kv_end < kTileKeys) ? last : -1;
+    c.kv_end = kv_end;
   }
 #pragma unroll
   for (int j = 0; j < Ctx::LPW_K; ++j) {
@@ -945,8 +1059,7 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     c.goff_v[j] = row * L::VROW + (2 * v_logical_slot<DV>(pc >> 1, row) + (pc & 1)) * 16;
   }
   int kro[8];
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) kro[kc] = L::K0 + r * L::KROW + (((2 * kc + g) ^ (r & 15)) * 16);
+  k_read_offsets<DV>(r, g, kro);
   int vro[NPV];
   {
     const int i16 = lane & 15, grp = lane >> 4;
@@ -959,14 +1072,11 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) bias_l[hh] = L::B0 + ((w * HPW + hh) * 8 + (r >> 4) * 4) * 4;
 
+  // the wave's first head in the block's first query row, and in this
+  // lane's row (rows past Sq read row Sq - 1)
+  const __bf16* qb = q + (((int64_t)b * Sq + qpos0) * kHeads + c.wave * HPW) * kD;
   bf16x8 qf[HPW][kD / 16];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const char* qrow = reinterpret_cast<const char*>(
-        q + (((int64_t)b * Sq + qpos0 + r) * kHeads + w * HPW + hh) * kD);
-#pragma unroll
-    for (int kc = 0; kc < kD / 16; ++kc) qf[hh][kc] = *reinterpret_cast<const bf16x8*>(qrow + (kc * 16 + 8 * g) * 2);
-  }
+  load_q<HPW>(qb + (int64_t)((TAIL ? min(qpos0 + r, Sq - 1) : qpos0 + r) - qpos0) * kHeads * kD, g, qf);
 
   f32x16 O[HPW][NPV];
   float rowsum[HPW];
@@ -978,8 +1088,8 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   }
 
   // ---- prologue: tiles 0 and 1 -------------------------------------------------
-  issue_tile<HPW, DV, 0>(smem, c, 0);
-  issue_tile<HPW, DV, 1>(smem, c, min(1, last));
+  issue_tile<HPW, DV, TAIL, 0>(smem, c, 0);
+  issue_tile<HPW, DV, TAIL, 1>(smem, c, min(1, last));
   tile_barrier();
 
   f32x16 S0[HPW], S1[HPW];
@@ -993,30 +1103,44 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
       mfma(S0[hh], kfrag<DV, 0>(smem, kro, 0, kc), qf[hh][kc]);
       mfma(S1[hh], kfrag<DV, 0>(smem, kro, 1, kc), qf[hh][kc]);
     }
-    softmax_capped<__bf16>(S0[hh], *reinterpret_cast<const f32x2*>(smem + bias_l[hh]) * beta_mul, alpha,
-                           den_a, rowsum[hh], P0[hh]);
+    softmax_capped<__bf16, TAIL>(S0[hh], *reinterpret_cast<const f32x2*>(smem + bias_l[hh]) * beta_mul,
+                                 alpha, den_a, rowsum[hh], P0[hh], klim - 8 * g);
   }
   bf16x8 ring[4];
 #pragma unroll
   for (int j = 0; j < 3; ++j) ring[j] = vfrag<DV, 0>(smem, vro, j, 0);
 
   // ---- main loop, unrolled over the three stages -------------------------------------
+  // A last tile that ends the sequence early (tile_end > 0) is left out of
+  // the pipeline (it is still prefetched with the others) and taken on its
+  // own at the end; with a single tile (tile_end == 0) the prologue and the
+  // tail mask it instead.
+  const int lastp = (TAIL && c.tile_end > 0) ? last - 1 : last;
   int t = 0;
   while (true) {
-    if (t >= last) break;
-    fast_iter<HPW, DV, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    if (t >= lastp) break;
+    fast_iter<HPW, DV, TAIL, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
-    if (t >= last) break;
-    fast_iter<HPW, DV, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    if (t >= lastp) break;
+    fast_iter<HPW, DV, TAIL, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
-    if (t >= last) break;
-    fast_iter<HPW, DV, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    if (t >= lastp) break;
+    fast_iter<HPW, DV, TAIL, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
   }
-  switch (last % 3) {
-    case 0: fast_tail<HPW, DV, 0>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
-    case 1: fast_tail<HPW, DV, 1>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
-    default: fast_tail<HPW, DV, 2>(smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+  switch (lastp % 3) {
+    case 0: fast_tail<HPW, DV, TAIL, 0>(klim - 64 * lastp - 32, smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    case 1: fast_tail<HPW, DV, TAIL, 1>(klim - 64 * lastp - 32, smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    default: fast_tail<HPW, DV, TAIL, 2>(klim - 64 * lastp - 32, smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+  }
+  if constexpr (TAIL) {
+    if (c.tile_end > 0) {  // uniform; the tile was loaded by the last iteration or the prologue
+      switch (last % 3) {
+        case 0: fast_partial<HPW, DV, 0>(klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
+        case 1: fast_partial<HPW, DV, 1>(klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
+        default: fast_partial<HPW, DV, 2>(klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
+      }
+    }
   }
   if constexpr (SPLIT) {
     // partial numerator rows [split][b][pos][h][DV] and denominators
@@ -1030,6 +1154,7 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
       const int h = w * HPW + hh;
       const float tot = rowsum[hh] + __shfl_xor(rowsum[hh], 32);
       float* nrow = wn + ((int64_t)(qpos0 + r) * kHeads + h) * DV + 4 * g;
+      if (TAIL && qpos0 + r >= Sq) continue;
 #pragma unroll
       for (int db = 0; db < NPV; ++db)
 #pragma unroll
@@ -1044,7 +1169,8 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) stage_output<__bf16, DV>(smem, O[hh], rowsum[hh], r, g, w * HPW + hh);
     __syncthreads();
-    copy_output<__bf16, NT, DV>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * DV, tid);
+    copy_output<__bf16, NT, DV>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * DV, tid,
+                                TAIL ? min(kBlockPos, Sq - qpos0) : kBlockPos);
   }
 }
 
@@ -1076,25 +1202,25 @@ void merge_partials_kernel(const float* __restrict__ ws, __bf16* __restrict__ ou
   *reinterpret_cast<u32x2*>(out + row * DV + 4 * c4) = wv;
 }
 
-template <int DV>
-hipError_t launch_fast(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
-                       float den_a) {
+template <int DV, bool TAIL>
+hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
+                         float den_a) {
   constexpr int HPW = kFastHeadsPerWave;
   const int splits = (int)a.kv_splits;
-  const int tiles = (int)(a.Sk / kTileKeys) / splits;
-  dim3 grid((unsigned)(a.Sq / kBlockPos), (unsigned)a.B, (unsigned)splits);
+  const int tiles = (int)((a.Sk + kTileKeys - 1) / kTileKeys) / splits;
+  dim3 grid((unsigned)((a.Sq + kBlockPos - 1) / kBlockPos), (unsigned)a.B, (unsigned)splits);
   const __bf16* q = static_cast<const __bf16*>(a.q);
   const __bf16* k = static_cast<const __bf16*>(a.k);
   const __bf16* v = static_cast<const __bf16*>(a.v);
   __bf16* out = static_cast<__bf16*>(a.out);
   if (splits == 1) {
-    hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, false>), grid,
+    hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, false, TAIL>), grid,
                        dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, out, nullptr,
                        (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
                        (int)a.bias_group, alpha, beta_mul, den_a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, true>), grid,
+  hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, true, TAIL>), grid,
                      dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, out, a.ws,
                      (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
                      (int)a.bias_group, alpha, beta_mul, den_a);
@@ -1105,6 +1231,14 @@ hipError_t launch_fast(const AttnLaunch& a, hipStream_t stream, float alpha, flo
   hipLaunchKernelGGL(merge_partials_kernel<DV>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, a.ws, out, rows, splits);
   return hipGetLastError();
+}
+
+template <int DV>
+hipError_t launch_fast(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
+                       float den_a) {
+  const bool tail = a.Sk % kTileKeys != 0 || a.Sq % kBlockPos != 0;
+  return tail ? launch_fast_t<DV, true>(a, stream, alpha, beta_mul, den_a)
+              : launch_fast_t<DV, false>(a, stream, alpha, beta_mul, den_a);
 }
 
 template <typename T, bool CAPPED>

@@ -76,7 +76,7 @@ class Shape:
 
     @property
     def P(self) -> int:
-        return self.S // BLOCK
+        return -(-self.S // BLOCK)
 
 
 SHAPES = {
@@ -143,7 +143,7 @@ def make_layer(name: str, layer: int = 0, *, hot: bool = False,
     """
     shp = SHAPES[name]
     S = shp.S if S is None else S
-    P = S // BLOCK
+    P = -(-S // BLOCK)  # a last cell shorter than 16 keeps its row and column
     seed = SEEDS[name] + layer + (HOT_SEED_OFFSET if hot else 0)
     rng = np.random.Generator(np.random.PCG64(seed))
     qkv_std = 1.0 if hot else 1.0 / math.sqrt(DK)
@@ -202,7 +202,7 @@ def make_custom(*, B: int, S: int, dtype: str, C: int = 16, seed: int = 0,
     n_pairs = B if n_pairs is None else n_pairs
     rng = np.random.Generator(np.random.PCG64(seed))
     f32 = np.float32
-    P = S // BLOCK
+    P = -(-S // BLOCK)  # a last cell shorter than 16 keeps its row and column
     q = rng.standard_normal((B, S, HQ, DK), dtype=f32) * f32(qkv_std)
     k = rng.standard_normal((B, S, 1, DK), dtype=f32) * f32(qkv_std)
     v = rng.standard_normal((B, S, 1, Dv), dtype=f32) * f32(qkv_std)

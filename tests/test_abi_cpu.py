@@ -58,8 +58,10 @@ ATTN_CASES = [
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL),
     (dict(bias=None), NULL), (dict(out=None), NULL),
     (dict(B=0), SHAPE), (dict(B=70000), SHAPE),
-    (dict(S=0), SHAPE), (dict(S=32), SHAPE), (dict(S=262144 + 64), SHAPE),
-    (dict(S=8192 + 16), UNSUP), (dict(S=100), UNSUP),
+    (dict(S=0), SHAPE), (dict(S=-64), SHAPE), (dict(S=262144 + 64), SHAPE),
+    # lengths off the 64-key tile: only the bf16 path with the cap takes them
+    (dict(S=8192 + 16, dtype=F32), UNSUP), (dict(S=100, softcap=0.0), UNSUP),
+    (dict(S=32, dtype=F32), UNSUP),
     (dict(Hq=4), UNSUP), (dict(Hq=16), UNSUP),
     # (every case here must stay invalid: the pointers are not device memory)
     (dict(Dk=64), UNSUP), (dict(Dv=64), UNSUP), (dict(Dv=256), UNSUP),
@@ -100,13 +102,15 @@ def attn_ex(**kw):
 
 # Every case must stay invalid: the pointers are not device memory.
 ATTN_EX_CASES = [
-    (dict(Sq=1000), UNSUP), (dict(Sq=16), SHAPE), (dict(Sq=8192 + 32), SHAPE),
+    (dict(Sq=1000, dtype=F32, kv_splits=1), UNSUP), (dict(Sq=0), SHAPE), (dict(Sq=8192 + 32), SHAPE),
     (dict(q_offset=8), UNSUP), (dict(q_offset=-16), SHAPE), (dict(q_offset=8192 - 1024 + 16), SHAPE),
     (dict(kv_splits=0), SHAPE), (dict(kv_splits=65), SHAPE), (dict(kv_splits=3), SHAPE),
     (dict(dtype=F32), UNSUP), (dict(softcap=0.0), UNSUP),
     (dict(ws=None), NULL), (dict(ws_bytes=1024), SHAPE), (dict(ws=WS + 8), ALIGN),
     (dict(ws=Q), ALIAS), (dict(ws=OUT - 1024), ALIAS),
-    (dict(Sk=8192 + 16), UNSUP), (dict(Dv=192, dtype=F32, kv_splits=1), UNSUP),
+    (dict(Sk=8192 + 16, dtype=F32, kv_splits=1), UNSUP), (dict(Dv=192, dtype=F32, kv_splits=1), UNSUP),
+    # 8192 + 16 keys make 129 tiles, which 8 ranges do not divide
+    (dict(Sk=8192 + 16), SHAPE), (dict(Sk=100, Sq=64, q_offset=0, kv_splits=4), SHAPE),
     (dict(q=None), NULL), (dict(out=Q), ALIAS),
 ]
 
@@ -128,6 +132,9 @@ def test_workspace_bytes():
     assert abg.auto_kv_splits(1, 8192, 8192) == 1
     assert abg.auto_kv_splits(1, 1024, 8192) == 8
     assert abg.auto_kv_splits(1, 64, 64) == 1
+    # ragged lengths: tiles = ceil(Sk / 64), query blocks = ceil(Sq / 32)
+    assert abg.auto_kv_splits(1, 1000, 1000) == 8  # 16 tiles, 32 query blocks: 8 x 32 = 256
+    assert abg.auto_kv_splits(1, 100, 100) == 2    # 2 tiles cap it
 
 
 def proj(**kw):

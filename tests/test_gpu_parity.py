@@ -238,6 +238,88 @@ def test_attention_splits_and_query_blocks(case):
     print(f"  splits {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Lengths off the tile grid (bf16 with the cap): S not a multiple of the
+# 64-key tile, Sq not a multiple of the 32-query block.  Keys past the end are
+# masked (p = 0); query rows past the end are computed and not stored.
+# ---------------------------------------------------------------------------
+TAILS = [
+    # B, S, Dv, q_rows (start, stop) or None, kv_splits
+    (1, 1, 128, None, 1),            # one key, one query
+    (1, 17, 128, None, 1),           # one tile, its last key in the first half
+    (2, 48, 128, None, 1),           # one tile, its last key in the second half
+    (1, 100, 128, None, 1),          # the partial tile in LDS stage 1
+    (1, 150, 128, None, 1),          # ... stage 2
+    (1, 200, 128, None, 1),          # ... stage 0 (after 3 whole tiles)
+    (1, 1000, 128, None, 1),         # 16 tiles; Sq % 32 = 8
+    (1, 1050, 128, None, 1),         # 17 tiles
+    (1, 1100, 128, None, 1),         # 18 tiles
+    (1, 1000, 128, None, 4),         # key ranges of 4 tiles
+    (1, 1000, 128, None, 8),         # ranges of 2 tiles
+    (1, 1000, 128, None, 16),        # one tile per range: the last is the partial one
+    (1, 1100, 128, None, 3),         # ranges of 6 tiles
+    (2, 777, 128, None, 1),          # two items with their own bias blocks
+    (1, 1000, 128, (16, 61), 1),     # 45 queries at an offset
+    (1, 1000, 128, (960, 1000), 2),  # the last 40 queries, 2 key ranges
+    (1, 64, 128, (32, 45), 1),       # whole tiles, 13 queries
+    (1, 333, 192, None, 1),
+    (1, 1000, 192, (496, 1000), 4),
+]
+
+
+@pytest.mark.parametrize("case", TAILS, ids=lambda c: "B%d_S%d_dv%d_q%s_z%s" % c)
+def test_attention_tails(case):
+    B, S, Dv, qr, z = case
+    L = workloads.make_custom(B=B, S=S, dtype="bf16", C=32, seed=900 + S + B, qkv_std=1.0,
+                              bias_std=2.0, Dv=Dv)
+    rows = range(0, S) if qr is None else range(*qr)
+    Sq = rows.stop - rows.start
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    assert tuple(bias.shape[1:]) == (8, -(-S // 16), -(-S // 16))
+    q = t["q"][:, rows.start:rows.stop].contiguous()
+    # with one item the output is a view of a larger buffer whose extra rows
+    # must come back untouched
+    pad = 7
+    buf = torch.full((B, Sq + pad, 8, Dv), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out_t = buf[:, :Sq] if B == 1 else torch.empty((B, Sq, 8, Dv), dtype=torch.bfloat16, device="cuda")
+    biased_mqa_fwd(q, t["k"], t["v"], bias, out_t, scale=L.scale, softcap=L.cap,
+                   q_offset=rows.start, kv_splits=z)
+    torch.cuda.synchronize()
+    if B == 1:
+        assert torch.isnan(buf[:, Sq:].float()).all(), "rows past Sq were written"
+    out = to_host(out_t)
+    bias64 = _oracle_bias(L)
+    worst = (0.0, 0.0)
+    for b in range(B):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, np.arange(rows.start, rows.stop),
+                                    scale=L.scale, cap=L.cap, bias_index=L.bias_index, batch=b)
+        ok, ma, rel = attention_ok(out[b], ref, "bf16")
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+        worst = (max(worst[0], ma), max(worst[1], rel))
+    print(f"  tails {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
+
+
+def test_single_key_returns_its_value():
+    """S = 1: every query attends to the one key with weight 1, so the output
+    is that key's value row (rounded to bf16 it is exact)."""
+    L = workloads.make_custom(B=3, S=1, dtype="bf16", C=8, seed=5, qkv_std=1.0, Dv=128)
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    out = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, softcap=5.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, t["v"].expand(3, 1, 8, 128))
+
+
+@pytest.mark.parametrize("S", [8191, 8000])
+def test_attention_tails_full_sampled(S):
+    """Near the full length, off the tile grid, sampled rows (the last ones
+    included)."""
+    L = workloads.make_custom(B=1, S=S, dtype="bf16", C=128, seed=S, qkv_std=1.0, bias_std=2.0)
+    _, out = _run_layer(L, "cuda")
+    _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=3))
+
+
 @pytest.mark.parametrize("dt,cap", [("f32", 5.0), ("bf16", 0.0)])
 def test_query_block_generic_kernel(dt, cap):
     """A query block at an offset on the float32 / uncapped kernel."""

@@ -171,6 +171,34 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
                                  int64_t kv_splits, float scale, float softcap,
                                  abg_dtype dtype, void* stream);
 
+/* abg_biased_mqa_fwd_ex with the bias projected inside the attention kernel
+ * from the pair representation, so that the compact bias is never written
+ * out (page "Making Full-Context AlphaGenome Fit on an RTX 3090", section
+ * "Why stock FlashAttention was not a drop-in replacement": the bias is the
+ * pair representation projected per head, one value per 16 x 16 block).
+ * Each workgroup projects, tile by tile, the cells its queries and keys
+ * use: cell (p, c) of head h is sum_ch pair[p, c, ch] * weight[ch, h], bf16
+ * products summed in float32 -- the value abg_pair_bias_project writes.
+ *
+ *   pair    [., P, P, C]  bf16, P = ceil(Sk/16); batch item b reads the
+ *           block at  pair + (b / pair_group) * pair_batch_stride
+ *           (elements; 0 shares one block by every item)
+ *   weight  [C, Hq]       bf16
+ *
+ * Limits beyond abg_biased_mqa_fwd_ex's: dtype ABG_BF16 with softcap > 0;
+ * Dv == 128; C == 128; pair_batch_stride 0 or >= P*P*C and a multiple of 8;
+ * 1 <= pair_group <= B; pair and weight 16-byte aligned and not overlapping
+ * out or the workspace.  kv_splits, q_offset and the workspace work as for
+ * abg_biased_mqa_fwd_ex. */
+abg_status abg_pair_biased_mqa_fwd(const void* q, const void* k, const void* v,
+                                   const void* pair, const void* weight, void* out,
+                                   void* workspace, int64_t workspace_bytes,
+                                   int64_t B, int64_t Sq, int64_t Sk, int64_t q_offset,
+                                   int64_t Hq, int64_t Dk, int64_t Dv, int64_t C,
+                                   int64_t pair_batch_stride, int64_t pair_group,
+                                   int64_t kv_splits, float scale, float softcap,
+                                   abg_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

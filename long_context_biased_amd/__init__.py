@@ -8,6 +8,7 @@ thin Python binding.
     from long_context_biased_amd import pair_bias_project, biased_mqa_fwd
     bias = pair_bias_project(pair, weight)          # [8, P, P] float32
     out = biased_mqa_fwd(q, k, v, bias, softcap=5.0)
+    out = pair_biased_mqa_fwd(q, k, v, pair, weight)  # the projection inside
 """
 
 from ._lib import (  # noqa: F401
@@ -20,8 +21,10 @@ from ._lib import (  # noqa: F401
     biased_mqa_fwd,
     load,
     pair_bias_project,
+    pair_biased_mqa_fwd,
     raw_biased_mqa_fwd,
     raw_biased_mqa_fwd_ex,
     raw_pair_bias_project,
+    raw_pair_biased_mqa_fwd,
     workspace_bytes,
 )

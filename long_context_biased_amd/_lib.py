@@ -25,7 +25,7 @@ STATUS = {0: "ABG_OK", 1: "ABG_ERR_NULL", 2: "ABG_ERR_SHAPE", 3: "ABG_ERR_UNSUPP
 #: Every symbol include/abg.h declares.
 EXPORTS = ("abg_abi_version", "abg_status_string", "abg_last_error",
            "abg_pair_bias_project", "abg_biased_mqa_fwd", "abg_biased_mqa_fwd_ex",
-           "abg_biased_mqa_fwd_workspace_bytes")
+           "abg_biased_mqa_fwd_workspace_bytes", "abg_pair_biased_mqa_fwd")
 
 
 class AbgError(RuntimeError):
@@ -66,6 +66,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           i64, i64, i64, i64, i64, i64, f32, f32, i32, vp]
     lib.abg_biased_mqa_fwd_workspace_bytes.restype = i64
     lib.abg_biased_mqa_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.abg_pair_biased_mqa_fwd.restype = i32
+    lib.abg_pair_biased_mqa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                            i64, i64, i64, i64, i64, i64, i64, f32, f32, i32, vp]
     _lib = lib
     return lib
 
@@ -96,6 +99,14 @@ def raw_biased_mqa_fwd_ex(q, k, v, bias, out, workspace, workspace_bytes, B, Sq,
     return load().abg_biased_mqa_fwd_ex(q, k, v, bias, out, workspace, workspace_bytes, B, Sq,
                                         Sk, q_offset, Hq, Dk, Dv, bias_batch_stride,
                                         bias_group, kv_splits, scale, softcap, dtype, stream)
+
+
+def raw_pair_biased_mqa_fwd(q, k, v, pair, weight, out, workspace, workspace_bytes, B, Sq, Sk,
+                            q_offset, Hq, Dk, Dv, C, pair_batch_stride, pair_group, kv_splits,
+                            scale, softcap, dtype, stream=None) -> int:
+    return load().abg_pair_biased_mqa_fwd(q, k, v, pair, weight, out, workspace, workspace_bytes,
+                                          B, Sq, Sk, q_offset, Hq, Dk, Dv, C, pair_batch_stride,
+                                          pair_group, kv_splits, scale, softcap, dtype, stream)
 
 
 def workspace_bytes(B, Sq, Hq, Dv, kv_splits) -> int:
@@ -237,4 +248,59 @@ def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
                                  out.data_ptr(), ws_ptr, ws_bytes, B, Sq, Sk, int(q_offset), Hq,
                                  Dk, Dv, bias_stride, bias_group, kv_splits, float(scale),
                                  float(softcap), _dtype_code(q), _stream(q.device)))
+    return out
+
+
+def pair_biased_mqa_fwd(q, k, v, pair, weight, out=None, *, scale: Optional[float] = None,
+                        softcap: float = 5.0, pair_group: int = 1, q_offset: int = 0,
+                        kv_splits=1, workspace=None):
+    """``biased_mqa_fwd`` with the bias projected inside the attention kernel
+    from ``pair`` [P, P, 128] or [Bp, P, P, 128] and ``weight`` [128, 8] (both
+    bfloat16; P = ceil(Sk/16)), so that no bias tensor is ever written.  Item
+    b reads pair block b // pair_group.  bfloat16 inputs with the cap, value
+    width 128.  Returns ``out`` [B, Sq, 8, 128].
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (pair, "pair"), (weight, "weight")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, S, heads, D]")
+    B, Sq, Hq, Dk = q.shape
+    Sk = k.shape[1]
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, Sk, 1, Dk) or tuple(v.shape[:3]) != (B, Sk, 1):
+        raise ValueError(f"k must be [B,Sk,1,Dk] and v [B,Sk,1,Dv]; got {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype == pair.dtype == weight.dtype):
+        raise TypeError("q, k, v, pair and weight must share a dtype")
+    P = (Sk + 15) // 16
+    p4 = pair.unsqueeze(0) if pair.dim() == 3 else pair
+    if p4.dim() != 4 or tuple(p4.shape[1:3]) != (P, P):
+        raise ValueError(f"pair must be [P, P, C] or [Bp, P, P, C] with P = {P}, got {tuple(pair.shape)}")
+    C = p4.shape[3]
+    if tuple(weight.shape) != (C, Hq):
+        raise ValueError(f"weight must be [{C}, {Hq}], got {tuple(weight.shape)}")
+    if p4.shape[0] > 1 and p4.shape[0] * pair_group < B:
+        raise ValueError("pair has too few items for B and pair_group")
+    pair_stride = 0 if p4.shape[0] == 1 else P * P * C
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out")
+    if out.dtype != q.dtype or tuple(out.shape) != (B, Sq, Hq, Dv):
+        raise ValueError("out must match q's dtype and be [B, Sq, Hq, Dv]")
+    if kv_splits == "auto":
+        kv_splits = auto_kv_splits(B, Sq, Sk)
+    kv_splits = int(kv_splits)
+    need = workspace_bytes(B, Sq, Hq, Dv, kv_splits) if kv_splits >= 1 else 0
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(raw_pair_biased_mqa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), p4.data_ptr(),
+                                   weight.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes, B, Sq, Sk,
+                                   int(q_offset), Hq, Dk, Dv, C, pair_stride, pair_group, kv_splits,
+                                   float(scale), float(softcap), _dtype_code(q), _stream(q.device)))
     return out

@@ -41,6 +41,117 @@ abg_status device_status(hipError_t e, const char* what) {
   return fail(ABG_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+// Validation and launch shared by the attention entry points: the bias
+// comes either compact (bias, float32 [., Hq, P, P]) or as the pair
+// representation and projection weight it is projected from (pair, bf16
+// [., P, P, C], and weight [C, Hq]); bias_batch_stride and bias_group then
+// describe pair.
+abg_status attention(const void* q, const void* k, const void* v, const float* bias,
+                     const void* pair, const void* weight, int64_t C, void* out,
+                     void* workspace, int64_t workspace_bytes, int64_t B, int64_t Sq,
+                     int64_t Sk, int64_t q_offset, int64_t Hq, int64_t Dk, int64_t Dv,
+                     int64_t bias_batch_stride, int64_t bias_group, int64_t kv_splits,
+                     float scale, float softcap, abg_dtype dtype, void* stream) {
+  if (dtype != ABG_F32 && dtype != ABG_BF16)
+    return fail(ABG_ERR_VALUE, "dtype %d is not ABG_F32 or ABG_BF16", (int)dtype);
+  if (!q) return fail(ABG_ERR_NULL, "q is NULL");
+  if (!k) return fail(ABG_ERR_NULL, "k is NULL");
+  if (!v) return fail(ABG_ERR_NULL, "v is NULL");
+  if (!out) return fail(ABG_ERR_NULL, "out is NULL");
+  if (B < 1 || B > 65535) return fail(ABG_ERR_SHAPE, "B = %lld must be in [1, 65535]", (long long)B);
+  if (!std::isfinite(softcap) || softcap < 0.f)
+    return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
+  // the bf16 path with the cap takes any length; the others whole tiles
+  const bool fast = dtype == ABG_BF16 && softcap > 0.f;
+  if (Sk < 1 || Sk > 262144)
+    return fail(ABG_ERR_SHAPE, "S = %lld must be in [1, 262144]", (long long)Sk);
+  if (!fast && Sk % 64 != 0)
+    return fail(ABG_ERR_UNSUPPORTED,
+                "S = %lld: lengths that are not a multiple of 64 are implemented for bf16 inputs with "
+                "softcap > 0 only", (long long)Sk);
+  if (Sq < 1 || Sq > Sk)
+    return fail(ABG_ERR_SHAPE, "Sq = %lld must be in [1, Sk = %lld]", (long long)Sq, (long long)Sk);
+  if (!fast && Sq % 32 != 0)
+    return fail(ABG_ERR_UNSUPPORTED,
+                "Sq = %lld: query counts that are not a multiple of 32 are implemented for bf16 inputs "
+                "with softcap > 0 only", (long long)Sq);
+  if (q_offset < 0 || q_offset > Sk - Sq)
+    return fail(ABG_ERR_SHAPE, "q_offset = %lld must be in [0, Sk - Sq = %lld]", (long long)q_offset,
+                (long long)(Sk - Sq));
+  if (q_offset % 16 != 0)
+    return fail(ABG_ERR_UNSUPPORTED, "q_offset = %lld must be a multiple of 16", (long long)q_offset);
+  if (Hq != 8) return fail(ABG_ERR_UNSUPPORTED, "Hq = %lld: only 8 query heads are supported", (long long)Hq);
+  if (Dk != 128) return fail(ABG_ERR_UNSUPPORTED, "Dk = %lld: only 128 is supported", (long long)Dk);
+  if (Dv != 128 && Dv != 192)
+    return fail(ABG_ERR_UNSUPPORTED, "Dv = %lld: only 128 and 192 are supported", (long long)Dv);
+  if (!std::isfinite(scale)) return fail(ABG_ERR_VALUE, "scale is not finite");
+  if (Dv == 192 && !fast)
+    return fail(ABG_ERR_UNSUPPORTED, "Dv = 192 is implemented for bf16 inputs with softcap > 0 only");
+  if (kv_splits < 1 || kv_splits > 64)
+    return fail(ABG_ERR_SHAPE, "kv_splits = %lld must be in [1, 64]", (long long)kv_splits);
+  const int64_t tiles = (Sk + 63) / 64;
+  if (tiles % kv_splits != 0)
+    return fail(ABG_ERR_SHAPE, "kv_splits = %lld must divide the %lld key tiles", (long long)kv_splits,
+                (long long)tiles);
+  if (kv_splits > 1 && !fast)
+    return fail(ABG_ERR_UNSUPPORTED, "kv_splits > 1 is implemented for bf16 inputs with softcap > 0 only");
+  const int64_t ws_need = abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits);
+  if (kv_splits > 1 && !workspace) return fail(ABG_ERR_NULL, "workspace is NULL (kv_splits > 1)");
+  if (kv_splits > 1 && workspace_bytes < ws_need)
+    return fail(ABG_ERR_SHAPE, "workspace_bytes = %lld, need %lld", (long long)workspace_bytes,
+                (long long)ws_need);
+  if (bias_group < 1 || bias_group > B)
+    return fail(ABG_ERR_SHAPE, "%s_group = %lld must be in [1, B]", pair ? "pair" : "bias",
+                (long long)bias_group);
+  const int64_t P = (Sk + 15) / 16;  // compact bias cells per side
+  if (pair) {
+    // the projection inside the attention kernel: its fast path only
+    if (!fast || Dv != 128)
+      return fail(ABG_ERR_UNSUPPORTED,
+                  "the pair form is implemented for ABG_BF16 with softcap > 0 and Dv = 128 only");
+    if (C != 128) return fail(ABG_ERR_UNSUPPORTED, "C = %lld: only 128 pair channels are supported", (long long)C);
+  }
+  // per-item block of the bias (elements) or of the pair representation
+  const int64_t bias_elems = pair ? P * P * C : Hq * P * P;
+  if (bias_batch_stride != 0 && bias_batch_stride < bias_elems)
+    return fail(ABG_ERR_SHAPE, "%s_batch_stride = %lld must be 0 or >= %lld", pair ? "pair" : "bias",
+                (long long)bias_batch_stride, (long long)bias_elems);
+  if (bias_batch_stride % (pair ? 8 : 4) != 0)
+    return fail(ABG_ERR_ALIGN, "%s_batch_stride must be a multiple of %d elements", pair ? "pair" : "bias",
+                pair ? 8 : 4);
+  const void* bsrc = pair ? pair : static_cast<const void*>(bias);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bsrc) || !aligned16(out))
+    return fail(ABG_ERR_ALIGN, "q, k, v, %s and out must be 16-byte aligned", pair ? "pair" : "bias");
+  if (pair && !aligned16(weight)) return fail(ABG_ERR_ALIGN, "weight must be 16-byte aligned");
+  if (kv_splits > 1 && !aligned16(workspace))
+    return fail(ABG_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const int64_t E = elem_bytes(dtype);
+  const int64_t q_bytes = B * Sq * Hq * Dk * E;
+  const int64_t kv_bytes = B * Sk * Dk * E;
+  const int64_t n_bias = (B - 1) / bias_group + 1;
+  const int64_t bias_bytes = ((n_bias - 1) * bias_batch_stride + bias_elems) * (pair ? 2 : 4);
+  const int64_t w_bytes = pair ? C * Hq * 2 : 0;
+  const int64_t out_bytes = B * Sq * Hq * Dv * E;
+  if (overlaps(out, out_bytes, q, q_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps q");
+  if (overlaps(out, out_bytes, k, kv_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps k");
+  if (overlaps(out, out_bytes, v, B * Sk * Dv * E)) return fail(ABG_ERR_ALIAS, "out overlaps v");
+  if (overlaps(out, out_bytes, bsrc, bias_bytes))
+    return fail(ABG_ERR_ALIAS, "out overlaps %s", pair ? "pair" : "bias");
+  if (pair && overlaps(out, out_bytes, weight, w_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps weight");
+  if (kv_splits > 1) {
+    const void* ins[6] = {q, k, v, bsrc, out, weight};
+    const int64_t sz[6] = {q_bytes, kv_bytes, B * Sk * Dv * E, bias_bytes, out_bytes, w_bytes};
+    for (int i = 0; i < (pair ? 6 : 5); ++i)
+      if (overlaps(workspace, ws_need, ins[i], sz[i]))
+        return fail(ABG_ERR_ALIAS, "workspace overlaps an input or the output");
+  }
+
+  abg::AttnLaunch a{q, k, v, bias, pair, weight, out, static_cast<float*>(workspace), B, Sq, Sk,
+                    q_offset, Dv, bias_batch_stride, bias_group, kv_splits, scale, softcap, dtype};
+  hipError_t e = abg::launch_biased_mqa_fwd(a, static_cast<hipStream_t>(stream));
+  return device_status(e, "biased_mqa_fwd launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,90 +230,26 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
                                  int64_t kv_splits, float scale, float softcap,
                                  abg_dtype dtype, void* stream) {
   g_last_error.clear();
-  if (dtype != ABG_F32 && dtype != ABG_BF16)
-    return fail(ABG_ERR_VALUE, "dtype %d is not ABG_F32 or ABG_BF16", (int)dtype);
-  if (!q) return fail(ABG_ERR_NULL, "q is NULL");
-  if (!k) return fail(ABG_ERR_NULL, "k is NULL");
-  if (!v) return fail(ABG_ERR_NULL, "v is NULL");
   if (!bias) return fail(ABG_ERR_NULL, "bias is NULL");
-  if (!out) return fail(ABG_ERR_NULL, "out is NULL");
-  if (B < 1 || B > 65535) return fail(ABG_ERR_SHAPE, "B = %lld must be in [1, 65535]", (long long)B);
-  if (!std::isfinite(softcap) || softcap < 0.f)
-    return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
-  // the bf16 path with the cap takes any length; the others whole tiles
-  const bool fast = dtype == ABG_BF16 && softcap > 0.f;
-  if (Sk < 1 || Sk > 262144)
-    return fail(ABG_ERR_SHAPE, "S = %lld must be in [1, 262144]", (long long)Sk);
-  if (!fast && Sk % 64 != 0)
-    return fail(ABG_ERR_UNSUPPORTED,
-                "S = %lld: lengths that are not a multiple of 64 are implemented for bf16 inputs with "
-                "softcap > 0 only", (long long)Sk);
-  if (Sq < 1 || Sq > Sk)
-    return fail(ABG_ERR_SHAPE, "Sq = %lld must be in [1, Sk = %lld]", (long long)Sq, (long long)Sk);
-  if (!fast && Sq % 32 != 0)
-    return fail(ABG_ERR_UNSUPPORTED,
-                "Sq = %lld: query counts that are not a multiple of 32 are implemented for bf16 inputs "
-                "with softcap > 0 only", (long long)Sq);
-  if (q_offset < 0 || q_offset > Sk - Sq)
-    return fail(ABG_ERR_SHAPE, "q_offset = %lld must be in [0, Sk - Sq = %lld]", (long long)q_offset,
-                (long long)(Sk - Sq));
-  if (q_offset % 16 != 0)
-    return fail(ABG_ERR_UNSUPPORTED, "q_offset = %lld must be a multiple of 16", (long long)q_offset);
-  if (Hq != 8) return fail(ABG_ERR_UNSUPPORTED, "Hq = %lld: only 8 query heads are supported", (long long)Hq);
-  if (Dk != 128) return fail(ABG_ERR_UNSUPPORTED, "Dk = %lld: only 128 is supported", (long long)Dk);
-  if (Dv != 128 && Dv != 192)
-    return fail(ABG_ERR_UNSUPPORTED, "Dv = %lld: only 128 and 192 are supported", (long long)Dv);
-  if (!std::isfinite(scale)) return fail(ABG_ERR_VALUE, "scale is not finite");
-  if (Dv == 192 && !fast)
-    return fail(ABG_ERR_UNSUPPORTED, "Dv = 192 is implemented for bf16 inputs with softcap > 0 only");
-  if (kv_splits < 1 || kv_splits > 64)
-    return fail(ABG_ERR_SHAPE, "kv_splits = %lld must be in [1, 64]", (long long)kv_splits);
-  const int64_t tiles = (Sk + 63) / 64;
-  if (tiles % kv_splits != 0)
-    return fail(ABG_ERR_SHAPE, "kv_splits = %lld must divide the %lld key tiles", (long long)kv_splits,
-                (long long)tiles);
-  if (kv_splits > 1 && !fast)
-    return fail(ABG_ERR_UNSUPPORTED, "kv_splits > 1 is implemented for bf16 inputs with softcap > 0 only");
-  const int64_t ws_need = abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits);
-  if (kv_splits > 1 && !workspace) return fail(ABG_ERR_NULL, "workspace is NULL (kv_splits > 1)");
-  if (kv_splits > 1 && workspace_bytes < ws_need)
-    return fail(ABG_ERR_SHAPE, "workspace_bytes = %lld, need %lld", (long long)workspace_bytes,
-                (long long)ws_need);
-  if (bias_group < 1 || bias_group > B)
-    return fail(ABG_ERR_SHAPE, "bias_group = %lld must be in [1, B]", (long long)bias_group);
-  const int64_t P = (Sk + 15) / 16;  // compact bias cells per side
-  const int64_t bias_elems = Hq * P * P;
-  if (bias_batch_stride != 0 && bias_batch_stride < bias_elems)
-    return fail(ABG_ERR_SHAPE, "bias_batch_stride = %lld must be 0 or >= Hq*ceil(S/16)^2 = %lld",
-                (long long)bias_batch_stride, (long long)bias_elems);
-  if (bias_batch_stride % 4 != 0)
-    return fail(ABG_ERR_ALIGN, "bias_batch_stride must be a multiple of 4 elements");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(out))
-    return fail(ABG_ERR_ALIGN, "q, k, v, bias and out must be 16-byte aligned");
-  if (kv_splits > 1 && !aligned16(workspace))
-    return fail(ABG_ERR_ALIGN, "workspace must be 16-byte aligned");
-  const int64_t E = elem_bytes(dtype);
-  const int64_t q_bytes = B * Sq * Hq * Dk * E;
-  const int64_t kv_bytes = B * Sk * Dk * E;
-  const int64_t n_bias = (B - 1) / bias_group + 1;
-  const int64_t bias_bytes = ((n_bias - 1) * bias_batch_stride + bias_elems) * 4;
-  const int64_t out_bytes = B * Sq * Hq * Dv * E;
-  if (overlaps(out, out_bytes, q, q_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps q");
-  if (overlaps(out, out_bytes, k, kv_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps k");
-  if (overlaps(out, out_bytes, v, B * Sk * Dv * E)) return fail(ABG_ERR_ALIAS, "out overlaps v");
-  if (overlaps(out, out_bytes, bias, bias_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps bias");
-  if (kv_splits > 1) {
-    const void* ins[5] = {q, k, v, bias, out};
-    const int64_t sz[5] = {q_bytes, kv_bytes, B * Sk * Dv * E, bias_bytes, out_bytes};
-    for (int i = 0; i < 5; ++i)
-      if (overlaps(workspace, ws_need, ins[i], sz[i]))
-        return fail(ABG_ERR_ALIAS, "workspace overlaps an input or the output");
-  }
+  return attention(q, k, v, bias, nullptr, nullptr, 0, out, workspace, workspace_bytes, B, Sq, Sk,
+                   q_offset, Hq, Dk, Dv, bias_batch_stride, bias_group, kv_splits, scale, softcap,
+                   dtype, stream);
+}
 
-  abg::AttnLaunch a{q, k, v, bias, out, static_cast<float*>(workspace), B, Sq, Sk, q_offset, Dv,
-                    bias_batch_stride, bias_group, kv_splits, scale, softcap, dtype};
-  hipError_t e = abg::launch_biased_mqa_fwd(a, static_cast<hipStream_t>(stream));
-  return device_status(e, "biased_mqa_fwd launch");
+abg_status abg_pair_biased_mqa_fwd(const void* q, const void* k, const void* v,
+                                   const void* pair, const void* weight, void* out,
+                                   void* workspace, int64_t workspace_bytes,
+                                   int64_t B, int64_t Sq, int64_t Sk, int64_t q_offset,
+                                   int64_t Hq, int64_t Dk, int64_t Dv, int64_t C,
+                                   int64_t pair_batch_stride, int64_t pair_group,
+                                   int64_t kv_splits, float scale, float softcap,
+                                   abg_dtype dtype, void* stream) {
+  g_last_error.clear();
+  if (!pair) return fail(ABG_ERR_NULL, "pair is NULL");
+  if (!weight) return fail(ABG_ERR_NULL, "weight is NULL");
+  return attention(q, k, v, nullptr, pair, weight, C, out, workspace, workspace_bytes, B, Sq, Sk,
+                   q_offset, Hq, Dk, Dv, pair_batch_stride, pair_group, kv_splits, scale, softcap,
+                   dtype, stream);
 }
 
 }  // extern "C"

@@ -13,7 +13,10 @@ struct AttnLaunch {
   const void* q;
   const void* k;
   const void* v;
-  const float* bias;
+  const float* bias;          // compact bias, or NULL when pair is given
+  const void* pair;           // bf16 pair representation [., P, P, 128] whose
+                              // projection replaces bias (bf16, cap, Dv 128)
+  const void* weight;         // bf16 [128, 8] projection weight with pair
   void* out;
   float* ws;                  // fp32 partials when kv_splits > 1, else unused
   int64_t B;
@@ -21,7 +24,7 @@ struct AttnLaunch {
   int64_t Sk;                 // key positions (the sequence length)
   int64_t q_offset;           // position of q's first row in the sequence
   int64_t Dv;                 // 128, or 192 (bf16 with the cap)
-  int64_t bias_batch_stride;  // elements
+  int64_t bias_batch_stride;  // elements (of pair when pair is given)
   int64_t bias_group;
   int64_t kv_splits;          // key ranges computed by separate workgroups
   float scale;

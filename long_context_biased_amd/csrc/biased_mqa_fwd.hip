@@ -645,7 +645,11 @@ struct FP {
   static constexpr int V0 = 0;
   static constexpr int K0 = NBUF * VTILE;
   static constexpr int B0 = K0 + NBUF * KTILE;
-  static constexpr int SMEM = B0 + NBUF * 256;
+  // pair vectors of one tile when the bias is projected in the kernel: 2
+  // query cells x 4 key cells x 128 channels, bf16
+  static constexpr int PTILE = 2 * 4 * 128 * 2;
+  static constexpr int PR0 = B0 + NBUF * 256;
+  static constexpr int SMEM = PR0 + NBUF * PTILE;
   static_assert(SMEM >= kBlockPos * kHeads * DV * 2, "output staging fits in the tile buffers");
 };
 
@@ -802,7 +806,7 @@ __device__ __forceinline__ void lds_copy4(const float* addr, uint32_t lds) {
 #pragma clang diagnostic pop
 }
 
-template <int HPW, int DV>
+template <int HPW, int DV, bool FUSED>
 struct FastCtx {
   static constexpr int NW = kHeads / HPW;   // waves per workgroup
   // direct 16-byte loads per lane per tile: K, V
@@ -821,16 +825,24 @@ struct FastCtx {
   // largest cell offset from bias_lane that stays in the bias row.
   int tile_end, kv_end;
   int bias_cap;
+  // FUSED: waves 0 and 1 copy the pair vectors of query cell `wave` (row
+  // pr_base): lane l the 16 bytes (l & 15) of key cell pr_cell + 4 t (its
+  // vector l >> 4 of the tile), clamped to the last cell pm1.  wreg holds
+  // the projection weights this lane multiplies: W[16 (l & 7) + i][head]
+  // for i = 0..15, as bf16 pairs.
+  const char* pr_base;
+  int pr_cell, pm1;
+  uint32_t wreg[HPW][8];
   int wave;             // wave index (uniform)
   float beta_mul;       // factor of the bias in the exp2 argument
 };
 
 // Direct HBM -> LDS copy of K and V of tile t into stage S (LPW_K + LPW_V
 // loads per lane, 1 KiB per wave each) and of the tile's bias cells.
-template <int HPW, int DV, bool TAIL, int S>
-__device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV>& c, int t) {
+template <int HPW, int DV, bool TAIL, bool FUSED, int S>
+__device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV, FUSED>& c, int t) {
   using L = FP<DV>;
-  using Ctx = FastCtx<HPW, DV>;
+  using Ctx = FastCtx<HPW, DV, FUSED>;
   const char* kt = c.kb_ptr + (int64_t)t * L::KTILE;
   const char* vt = c.vb_ptr + (int64_t)t * L::VTILE;
   const uint32_t lds = (uint32_t)(size_t)(lds_void*)smem;
@@ -846,10 +858,18 @@ __device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV>& c
   for (int j = 0; j < Ctx::LPW_V; ++j)
     lds_copy16(vt, TAIL ? min(c.goff_v[j], vcap) : c.goff_v[j],
                lds + L::V0 + S * L::VTILE + (uint32_t)((Ctx::LPW_V * c.wave + j) * 1024));
-  // the tile's 64 compact-bias cells (8 heads x 2 query blocks x 4 key
-  // blocks), one per lane of wave 0
-  if (c.wave == 0)
-    lds_copy4(c.bias_lane + (TAIL ? min(4 * t, c.bias_cap) : 4 * t), lds + L::B0 + S * 256);
+  if constexpr (FUSED) {
+    // the tile's 8 pair vectors (2 query cells x 4 key cells, 1 KiB per
+    // query cell), projected by each wave for its heads once they arrive
+    if (c.wave < 2)
+      lds_copy16(c.pr_base, min(c.pr_cell + 4 * t, c.pm1) * 256 + (int)(threadIdx.x & 15) * 16,
+                 lds + L::PR0 + S * L::PTILE + c.wave * 1024);
+  } else {
+    // the tile's 64 compact-bias cells (8 heads x 2 query blocks x 4 key
+    // blocks), one per lane of wave 0
+    if (c.wave == 0)
+      lds_copy4(c.bias_lane + (TAIL ? min(4 * t, c.bias_cap) : 4 * t), lds + L::B0 + S * 256);
+  }
 }
 
 
@@ -858,6 +878,50 @@ __device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV>& c
 __device__ __forceinline__ void tile_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+}
+
+// Sum over each group of 8 lanes (every lane of the group gets the same
+// sum: each step adds the same two values in either order).
+__device__ __forceinline__ float sum8(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)); // row_half_mirror
+  return x;
+}
+
+// Compact-bias cells projected in the kernel.  For the tile in stage S,
+// cell (query cell qc, key cell kc) of head h is sum_c pair[qc, kc, c] W[c, h]
+// (bf16 products, float32 sums).  Lane l holds channels 16 (l & 7) .. + 15
+// of pair vector l >> 3 = 4 qc + kc (pair_load); the 8 lanes of a vector sum
+// it and all store the (identical) sum where the copied bias would be
+// (pair_store) -- no branch, which would split the stage's schedule.  Each
+// wave writes, and later reads, only its own heads' cells, so the in-order
+// LDS accesses of the wave suffice: no barrier.
+template <int DV, int S>
+__device__ __forceinline__ void pair_load(const char* smem, bf16x8 (&a)[2]) {
+  using L = FP<DV>;
+  const int lane = (int)threadIdx.x & 63;
+  const char* pt = smem + L::PR0 + S * L::PTILE + (lane >> 3) * 256 + (lane & 7) * 32;
+  a[0] = *reinterpret_cast<const bf16x8*>(pt);
+  a[1] = *reinterpret_cast<const bf16x8*>(pt + 16);
+}
+template <int HPW, int DV, int S>
+__device__ __forceinline__ void pair_store(char* smem, const bf16x8 (&a)[2], const uint32_t (&wreg)[HPW][8],
+                                           int wave) {
+  using L = FP<DV>;
+  const int lane = (int)threadIdx.x & 63;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    float s[2] = {0.f, 0.f};  // two chains, added at the end
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x2 w = __builtin_bit_cast(bf16x2, wreg[hh][i]);
+      const bf16x2 x = {a[i >> 2][2 * (i & 3)], a[i >> 2][2 * (i & 3) + 1]};
+      s[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(x, w, s[i & 1], false);
+    }
+    const float t = sum8(s[0] + s[1]);
+    reinterpret_cast<float*>(smem + L::B0 + S * 256)[(wave * HPW + hh) * 8 + (lane >> 3)] = t;
+  }
 }
 
 template <int HPW, int S>
@@ -869,8 +933,8 @@ __device__ __forceinline__ void read_beta(const char* smem, const int (&bias_l)[
 }
 
 // One pipelined iteration for tile t in stage C.
-template <int HPW, int DV, bool TAIL, int C>
-__device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV>& c, int t, int last,
+template <int HPW, int DV, bool TAIL, bool FUSED, int C>
+__device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUSED>& c, int t, int last,
                                           const int (&kro)[8], const int (&vro)[DV / 32],
                                           const int (&bias_l)[HPW], const bf16x8 (&qf)[HPW][8],
                                           f32x16 (&O)[HPW][DV / 32], f32x16 (&S0)[HPW],
@@ -880,12 +944,15 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV>& c,
   constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
   // tile t+2 into the stage that held tile t-1 (clamped past the end: the
   // copy lands in a stage nobody reads again)
-  issue_tile<HPW, DV, TAIL, NN>(smem, c, min(t + 2, last));
+  issue_tile<HPW, DV, TAIL, FUSED, NN>(smem, c, min(t + 2, last));
+  bf16x8 pv[2];
+  if constexpr (FUSED) pair_load<DV, NXT>(smem, pv);  // pair vectors of tile t+1, read during X
   f32x2 beta[HPW];
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
   read_beta<HPW, C>(smem, bias_l, 1, c.beta_mul, beta);
   fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, qf, O, S0, P0, S1, beta, alpha, den_a, rowsum, P1, ring);
   // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
+  if constexpr (FUSED) pair_store<HPW, DV, NXT>(smem, pv, c.wreg, c.wave);  // bias cells of tile t+1
   read_beta<HPW, NXT>(smem, bias_l, 0, c.beta_mul, beta);
   fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, qf, O, S1, P1, S0, beta, alpha, den_a, rowsum, P0, ring);
   tile_barrier();
@@ -947,8 +1014,9 @@ __device__ __forceinline__ void k_read_offsets(int r, int g, int (&kro)[8]) {
 // qpos0 of this workgroup (rows past Sq read row Sq - 1).  Q and the K
 // offsets are loaded again here rather than kept from the start: holding
 // them past the pipelined loop costs more registers than that loop leaves.
-template <int HPW, int DV, int C>
-__device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpos0, int Sq, const char* smem,
+template <int HPW, int DV, bool FUSED, int C>
+__device__ __forceinline__ void fast_partial(const FastCtx<HPW, DV, FUSED>& c, int lim0, const __bf16* qb,
+                                             int qpos0, int Sq, char* smem,
                                              const int (&vro)[DV / 32], const int (&bias_l)[HPW],
                                              f32x16 (&O)[HPW][DV / 32], float alpha, float beta_mul,
                                              float den_a, float (&rowsum)[HPW]) {
@@ -963,6 +1031,11 @@ __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpo
   int kro[8];
   k_read_offsets<DV>(lane & 31, g, kro);
   const int lim = lim0 - 8 * g;
+  if constexpr (FUSED) {  // bias cells of this tile
+    bf16x8 pv[2];
+    pair_load<DV, C>(smem, pv);
+    pair_store<HPW, DV, C>(smem, pv, c.wreg, c.wave);
+  }
   // QK of both halves first, so that Q and the K offsets are dead before
   // the value fragments are read
   f32x16 sc[2][HPW];
@@ -1001,16 +1074,17 @@ __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpo
 // ends the sequence is copied with its rows past the end clamped to its last
 // row and those keys masked (p = 0); query rows past Sq read row Sq - 1 and
 // store nothing.
-template <int HPW, int DV, bool SPLIT, bool TAIL>
+template <int HPW, int DV, bool SPLIT, bool TAIL, bool FUSED>
 __global__ __launch_bounds__(64 * (kHeads / HPW), 1)
 void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                        const __bf16* __restrict__ v, const float* __restrict__ bias,
+                                       const __bf16* __restrict__ pair, const __bf16* __restrict__ wt,
                                        __bf16* __restrict__ out, float* __restrict__ ws, int Sq,
                                        int S, int q_offset, int tiles_per_split,
                                        int64_t bias_batch_stride, int bias_group, float alpha,
                                        float beta_mul, float den_a) {
   using L = FP<DV>;
-  using Ctx = FastCtx<HPW, DV>;
+  using Ctx = FastCtx<HPW, DV, FUSED>;
   constexpr int NT = 64 * (kHeads / HPW);
   constexpr int NPV = DV / 32;
   __shared__ __attribute__((aligned(16))) char smem[L::SMEM];
@@ -1035,15 +1109,32 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   c.vb_ptr = reinterpret_cast<const char*>(v + ((int64_t)b * S + key0) * DV);
   c.beta_mul = beta_mul;
   c.wave = __builtin_amdgcn_readfirstlane(w);
-  {
+  c.tile_end = (TAIL && split == (int)gridDim.z - 1 && kv_end < kTileKeys) ? last : -1;
+  c.kv_end = kv_end;
+  if constexpr (!FUSED) {
     // bias cell of lane l: head l>>3, query block (l>>2)&1, key block l&3
     const int bh = lane >> 3, pb = (lane >> 2) & 1, cell = lane & 3;
     const int qrow = min((pos0 >> 4) + pb, P - 1);  // clamped: query rows past the end
     const float* row = bias + (int64_t)(b / bias_group) * bias_batch_stride + ((int64_t)bh * P + qrow) * P;
     c.bias_lane = row + cell + (key0 >> 4);
     c.bias_cap = P - 1 - cell - (int)(key0 >> 4);
-    c.tile_end = (TAIL && split == (int)gridDim.z - 1 && kv_end < kTileKeys) ? last : -1;
-    c.kv_end = kv_end;
+  }
+  if constexpr (FUSED) {
+    // pair [., P, P, 128] of this item: waves 0 and 1 copy query cell
+    // (pos0 >> 4) + wave (clamped), key cells from key0 >> 4 on
+    const int qc = min((pos0 >> 4) + min(c.wave, 1), P - 1);
+    c.pr_base = reinterpret_cast<const char*>(pair + (int64_t)(b / bias_group) * bias_batch_stride +
+                                              (int64_t)qc * P * 128);
+    c.pr_cell = (int)(key0 >> 4) + (lane >> 4);
+    c.pm1 = P - 1;
+    const unsigned short* w16 = reinterpret_cast<const unsigned short*>(wt);
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ch = 16 * (lane & 7) + 2 * i, h = c.wave * HPW + hh;
+        c.wreg[hh][i] = (uint32_t)w16[ch * kHeads + h] | ((uint32_t)w16[(ch + 1) * kHeads + h] << 16);
+      }
   }
 #pragma unroll
   for (int j = 0; j < Ctx::LPW_K; ++j) {
@@ -1088,9 +1179,14 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   }
 
   // ---- prologue: tiles 0 and 1 -------------------------------------------------
-  issue_tile<HPW, DV, TAIL, 0>(smem, c, 0);
-  issue_tile<HPW, DV, TAIL, 1>(smem, c, min(1, last));
+  issue_tile<HPW, DV, TAIL, FUSED, 0>(smem, c, 0);
+  issue_tile<HPW, DV, TAIL, FUSED, 1>(smem, c, min(1, last));
   tile_barrier();
+  if constexpr (FUSED) {  // bias cells of tile 0
+    bf16x8 pv[2];
+    pair_load<DV, 0>(smem, pv);
+    pair_store<HPW, DV, 0>(smem, pv, c.wreg, c.wave);
+  }
 
   f32x16 S0[HPW], S1[HPW];
   bf16x8 P0[HPW][2], P1[HPW][2];
@@ -1119,13 +1215,13 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   int t = 0;
   while (true) {
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
     ++t;
   }
   switch (lastp % 3) {
@@ -1136,9 +1232,9 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   if constexpr (TAIL) {
     if (c.tile_end > 0) {  // uniform; the tile was loaded by the last iteration or the prologue
       switch (last % 3) {
-        case 0: fast_partial<HPW, DV, 0>(klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
-        case 1: fast_partial<HPW, DV, 1>(klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
-        default: fast_partial<HPW, DV, 2>(klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
+        case 0: fast_partial<HPW, DV, FUSED, 0>(c, klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
+        case 1: fast_partial<HPW, DV, FUSED, 1>(c, klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
+        default: fast_partial<HPW, DV, FUSED, 2>(c, klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
       }
     }
   }
@@ -1202,7 +1298,7 @@ void merge_partials_kernel(const float* __restrict__ ws, __bf16* __restrict__ ou
   *reinterpret_cast<u32x2*>(out + row * DV + 4 * c4) = wv;
 }
 
-template <int DV, bool TAIL>
+template <int DV, bool TAIL, bool FUSED>
 hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
                          float den_a) {
   constexpr int HPW = kFastHeadsPerWave;
@@ -1213,15 +1309,17 @@ hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, f
   const __bf16* k = static_cast<const __bf16*>(a.k);
   const __bf16* v = static_cast<const __bf16*>(a.v);
   __bf16* out = static_cast<__bf16*>(a.out);
+  const __bf16* pair = static_cast<const __bf16*>(a.pair);
+  const __bf16* wt = static_cast<const __bf16*>(a.weight);
   if (splits == 1) {
-    hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, false, TAIL>), grid,
-                       dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, out, nullptr,
+    hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, false, TAIL, FUSED>), grid,
+                       dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, pair, wt, out, nullptr,
                        (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
                        (int)a.bias_group, alpha, beta_mul, den_a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, true, TAIL>), grid,
-                     dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, out, a.ws,
+  hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, true, TAIL, FUSED>), grid,
+                     dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, pair, wt, out, a.ws,
                      (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
                      (int)a.bias_group, alpha, beta_mul, den_a);
   const hipError_t e = hipGetLastError();
@@ -1237,8 +1335,13 @@ template <int DV>
 hipError_t launch_fast(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
                        float den_a) {
   const bool tail = a.Sk % kTileKeys != 0 || a.Sq % kBlockPos != 0;
-  return tail ? launch_fast_t<DV, true>(a, stream, alpha, beta_mul, den_a)
-              : launch_fast_t<DV, false>(a, stream, alpha, beta_mul, den_a);
+  if constexpr (DV == 128) {
+    if (a.pair)  // bias projected in the kernel from the pair representation
+      return tail ? launch_fast_t<DV, true, true>(a, stream, alpha, beta_mul, den_a)
+                  : launch_fast_t<DV, false, true>(a, stream, alpha, beta_mul, den_a);
+  }
+  return tail ? launch_fast_t<DV, true, false>(a, stream, alpha, beta_mul, den_a)
+              : launch_fast_t<DV, false, false>(a, stream, alpha, beta_mul, den_a);
 }
 
 template <typename T, bool CAPPED>

@@ -122,6 +122,42 @@ def test_attention_ex_rejects(kw, code):
     assert abg.load().abg_last_error().decode()
 
 
+def pattn(**kw):
+    a = dict(q=Q, k=K, v=V, pair=BIAS, weight=WS, out=OUT, ws=None, ws_bytes=0, B=1, Sq=8192,
+             Sk=8192, q_offset=0, Hq=8, Dk=128, Dv=128, C=128, pair_batch_stride=0, pair_group=1,
+             kv_splits=1, scale=0.088, softcap=5.0, dtype=BF16)
+    a.update(kw)
+    return abg.raw_pair_biased_mqa_fwd(a["q"], a["k"], a["v"], a["pair"], a["weight"], a["out"],
+                                       a["ws"], a["ws_bytes"], a["B"], a["Sq"], a["Sk"],
+                                       a["q_offset"], a["Hq"], a["Dk"], a["Dv"], a["C"],
+                                       a["pair_batch_stride"], a["pair_group"], a["kv_splits"],
+                                       a["scale"], a["softcap"], a["dtype"], None)
+
+
+# The pair form (projection inside the attention kernel).  Every case must
+# stay invalid: the pointers are not device memory.
+PAIR_CASES = [
+    (dict(pair=None), NULL), (dict(weight=None), NULL), (dict(q=None), NULL), (dict(out=None), NULL),
+    (dict(dtype=F32), UNSUP), (dict(softcap=0.0), UNSUP), (dict(Dv=192), UNSUP),
+    (dict(C=64), UNSUP), (dict(C=256), UNSUP), (dict(dtype=5), VALUE),
+    (dict(Sk=0), SHAPE), (dict(Sq=0), SHAPE), (dict(kv_splits=3), SHAPE),
+    (dict(kv_splits=8, ws=None), NULL),
+    (dict(B=2, pair_batch_stride=100), SHAPE), (dict(B=2, pair_batch_stride=512 * 512 * 128 + 4), ALIGN),
+    (dict(pair_group=0), SHAPE), (dict(B=2, pair_group=3), SHAPE),
+    (dict(pair=BIAS + 8), ALIGN), (dict(weight=WS + 2), ALIGN), (dict(out=OUT + 8), ALIGN),
+    (dict(out=BIAS), ALIAS), (dict(out=WS - 1024), ALIAS), (dict(out=Q), ALIAS),
+    (dict(kv_splits=8, ws=Q, ws_bytes=1 << 30), ALIAS),
+    (dict(kv_splits=8, ws=WS + 1024, ws_bytes=1 << 30), ALIAS),  # onto the 2 KiB weight
+]
+
+
+@pytest.mark.parametrize("kw,code", PAIR_CASES, ids=lambda x: str(x))
+def test_pair_attention_rejects(kw, code):
+    st = pattn(**kw)
+    assert st == code, (st, abg.load().abg_last_error())
+    assert abg.load().abg_last_error().decode()
+
+
 def test_workspace_bytes():
     assert abg.workspace_bytes(1, 2048, 8, 128, 1) == 0
     assert abg.workspace_bytes(2, 1024, 8, 128, 4) == 4 * 2 * 1024 * 8 * 129 * 4

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from gpu_util import sample_rows, to_gpu, to_host, upload
-from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, workloads
+from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, pair_biased_mqa_fwd, workloads
 from long_context_biased_amd import workspace_bytes as abg_workspace_bytes
 from parity import attention_ok, projection_ok
 
@@ -318,6 +318,70 @@ def test_attention_tails_full_sampled(S):
     L = workloads.make_custom(B=1, S=S, dtype="bf16", C=128, seed=S, qkv_std=1.0, bias_std=2.0)
     _, out = _run_layer(L, "cuda")
     _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=3))
+
+
+# ---------------------------------------------------------------------------
+# The projection inside the attention kernel (pair form): no bias tensor
+# ---------------------------------------------------------------------------
+PAIR = [
+    # B, S, q_rows (start, stop) or None, kv_splits, n_pairs
+    (1, 2048, None, 1, None),
+    (2, 512, None, 1, 1),            # two items share one pair block
+    (4, 256, None, 2, 2),            # pairs of items share a block (the variant's layout)
+    (1, 1000, None, 1, None),        # lengths off the tile grid
+    (1, 1000, None, 16, None),       # ... one tile per key range
+    (1, 100, None, 1, None),
+    (1, 17, None, 1, None),
+    (1, 2048, (512, 1024), 8, None),  # a query block at an offset, key ranges
+    (1, 1000, (16, 61), 1, None),
+]
+
+
+def _run_pair(L, rows, z):
+    t = upload(L)
+    q = t["q"][:, rows.start:rows.stop].contiguous()
+    out = pair_biased_mqa_fwd(q, t["k"], t["v"], t["pair"], t["weight"], scale=L.scale,
+                              softcap=L.cap, pair_group=L.bias_group, q_offset=rows.start,
+                              kv_splits=z)
+    # the same through the projection kernel and the compact bias
+    bias = pair_bias_project(t["pair"], t["weight"])
+    two = biased_mqa_fwd(q, t["k"], t["v"], bias, scale=L.scale, softcap=L.cap,
+                         bias_group=L.bias_group, q_offset=rows.start, kv_splits=z)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(two)
+
+
+@pytest.mark.parametrize("case", PAIR, ids=lambda c: "B%d_S%d_q%s_z%s_pairs%s" % c)
+def test_pair_form(case):
+    B, S, qr, z, n_pairs = case
+    L = workloads.make_custom(B=B, S=S, dtype="bf16", C=128, seed=700 + S + B, qkv_std=1.0,
+                              bias_std=2.0, n_pairs=n_pairs)
+    rows = range(0, S) if qr is None else range(*qr)
+    out, two = _run_pair(L, rows, z)
+    bias64 = _oracle_bias(L)
+    worst = (0.0, 0.0)
+    for b in range(B):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, np.arange(rows.start, rows.stop),
+                                    scale=L.scale, cap=L.cap, bias_index=L.bias_index, batch=b)
+        ok, ma, rel = attention_ok(out[b], ref, "bf16")
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+        worst = (max(worst[0], ma), max(worst[1], rel))
+    # the two routes differ only in the float32 summation order of the bias
+    diff = float(np.max(np.abs(out - two)))
+    assert diff <= 2e-2, diff
+    print(f"  pair form {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}; vs two kernels {diff:.3g}",
+          flush=True)
+
+
+@pytest.mark.parametrize("name,hot", [("full", False), ("full", True), ("variant", False)],
+                         ids=["full_base", "full_hot", "variant"])
+def test_pair_form_full_sampled(name, hot):
+    """The full-context and variant workloads through the pair form, sampled
+    rows (every item of the variant, whose ref/alt items share a pair)."""
+    L = workloads.make_layer(name, layer=2, hot=hot)
+    out, two = _run_pair(L, range(0, L.S), 1)
+    _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=21))
+    assert float(np.max(np.abs(out - two))) <= 2e-2
 
 
 @pytest.mark.parametrize("dt,cap", [("f32", 5.0), ("bf16", 0.0)])

@@ -2,18 +2,28 @@
 
 One step = the full-context workload: 9 independent seeded layers (one per
 transformer block), each = pair-bias projection ([512,512,128] bf16 ->
-[8,512,512] fp32) + biased soft-capped MQA forward (B=1, S=8192, 8 query
-heads, 1 K/V head, d=128, bf16 inputs, fp32 accumulation), back to back on
-one stream with every input already resident in HBM.
+8 heads of 512 x 512 cells) + biased soft-capped MQA forward (B=1, S=8192,
+8 query heads, 1 K/V head, d=128, bf16 inputs, fp32 accumulation), back to
+back on one stream with every input already resident in HBM.
+
+Two routes compute a layer: the pair form (default for d_v = 128), one
+kernel that projects the bias cells it uses inside the attention and never
+writes a bias tensor; and two kernels, the projection writing the compact
+fp32 bias and the attention reading it.  The route not timed is measured
+after it, for comparison.
+
+Before each route's W warmup steps it runs untimed steps for --settle-ms
+(300 ms): under sustained load the clock takes tens of milliseconds to
+settle, and a route timed before that reads slow.
 
 Prints ONE JSON line: attention TFLOP/s over the whole step (FLOPs =
 2*B*Hq*S^2*(Dk + Dv) per layer, non-causal QK^T + PV), the roofline of the dominant
-kernel (the attention) from HIP events on its own stream, and the CPU oracle
-timed on a bounded sample (3 of the 9 layers by default) on this host's cores.
+kernel from HIP events on its own stream, and the CPU oracle timed on a
+bounded sample (3 of the 9 layers by default) on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--cpu-layers N]
                     [--dv 128|192] [--workload full|mid|shard] [--kv-splits N|auto]
-                    [--copy-mib N]
+                    [--path pair|two] [--settle-ms T] [--copy-mib N]
 """
 
 from __future__ import annotations
@@ -50,6 +60,10 @@ def proj_bytes(P, C, H=8, elem=2):
     return P * P * C * elem + C * H * elem + H * P * P * 4
 
 
+def proj_flops(P, C, H=8):
+    return 2.0 * P * P * C * H
+
+
 def source_digest():
     import hashlib
     h = hashlib.sha256()
@@ -59,10 +73,11 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_counters():
-    """HBM bytes and MFMA counters per attention launch from the committed
-    rocprofv3 summary, if it was taken on the current kernel source; else
-    None."""
+def load_counters(path):
+    """HBM bytes and MFMA counters per launch of the timed kernel (the pair
+    form, or the attention of the two-kernel route) from the committed
+    rocprofv3 summary, if it was taken on the current kernel source and
+    route; else None."""
     try:
         kv = {}
         with open(COUNTERS_FILE) as f:
@@ -70,7 +85,7 @@ def load_counters():
                 if "=" in line and not line.lstrip().startswith("#"):
                     k, v = line.split("=", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("source_digest") != source_digest():
+        if kv.get("source_digest") != source_digest() or kv.get("path", "two") != path:
             return None
         return {"hbm_bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
                 "mfma_flops_per_launch": float(kv["mfma_flops_per_launch"]),
@@ -122,6 +137,13 @@ def main():
     ap.add_argument("--kv-splits", default=None,
                     help="key ranges per attention call (an integer or 'auto'; default: 1 for "
                          "full, auto otherwise)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before each route's warmup steps, run untimed steps for this long: "
+                         "the clock takes tens of ms of sustained load to settle, and a route "
+                         "timed while it still moves reads up to 30%% slow")
+    ap.add_argument("--path", default=None, choices=("pair", "two"),
+                    help="pair: the projection inside the attention kernel (default for dv "
+                         "128); two: projection kernel + attention kernel (default for dv 192)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 3 plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -131,8 +153,14 @@ def main():
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    path = args.path or ("pair" if args.dv == 128 else "two")
+    if path == "pair" and args.dv != 128:
+        print("the pair form is implemented for dv 128 only", file=sys.stderr)
+        sys.exit(2)
+
     import torch
-    from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, workloads
+    from long_context_biased_amd import (biased_mqa_fwd, pair_bias_project, pair_biased_mqa_fwd,
+                                         workloads)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -178,7 +206,7 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(events=None):
+    def step_two(events=None):
         for li, t in enumerate(layers):
             if events is not None:
                 events[li][0].record(stream)
@@ -191,42 +219,72 @@ def main():
             if events is not None:
                 events[li][2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def step_pair(events=None):
+        for li, t in enumerate(layers):
+            if events is not None:
+                events[li][0].record(stream)
+            pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], out=t["out"],
+                                scale=scale, softcap=cap, q_offset=t["q_off"],
+                                kv_splits=t["z"], workspace=t["ws"])
+            if events is not None:
+                events[li][1].record(stream)
+                events[li][2].record(stream)
 
-    # Timed region: K steps between two events, no per-kernel events inside.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-
-    # Per-kernel durations: the same steps again, each launch bracketed by
-    # events on the launch stream.
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_layers)]
-          for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    proj_ms = [e[0].elapsed_time(e[1]) for st in ev for e in st]
-    attn_ms = [e[1].elapsed_time(e[2]) for st in ev for e in st]
-    attn_avg = float(np.mean(attn_ms))
-    proj_avg = float(np.mean(proj_ms))
+    def measure(step):
+        """ms per step over K timed steps (after W warmups), then per-kernel
+        averages from the same steps run again with events around each
+        launch: (ms_per_step, first-kernel ms list, second-kernel ms list)."""
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        while time.perf_counter() < t_end:  # clock settle, untimed
+            step()
+            torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        # Timed region: K steps between two events, no per-kernel events inside.
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_layers)]
+              for _ in range(args.steps)]
+        for st in range(args.steps):
+            step(ev[st])
+        torch.cuda.synchronize()
+        k1 = [e[0].elapsed_time(e[1]) for st in ev for e in st]
+        k2 = [e[1].elapsed_time(e[2]) for st in ev for e in st]
+        return ms, k1, k2
 
     Sq = layers[0]["Sq"]
     fl_layer = attn_flops(1, S, Dv=args.dv, Sq=Sq)
-    value = n_layers * fl_layer / (ms_per_step * 1e-3) / 1e12
-    achieved = fl_layer / (attn_avg * 1e-3) / 1e12
-    counters = load_counters() if (args.dv == 128 and wl == "full") else None
     pb = proj_bytes(P, 128)
-    log(f"step {ms_per_step:.3f} ms; attention avg {attn_avg * 1e3:.1f} us "
-        f"(median {np.median(attn_ms) * 1e3:.1f}, p95 {np.percentile(attn_ms, 95) * 1e3:.1f}) "
-        f"= {achieved:.1f} TFLOP/s; projection avg {proj_avg * 1e3:.1f} us = "
-        f"{pb / (proj_avg * 1e-3) / 1e9:.0f} GB/s")
+    pf = proj_flops(P, 128)
+    if path == "pair":
+        ms_per_step, fused_ms, _ = measure(step_pair)
+        kern_ms = fused_ms
+        kern_fl = fl_layer + pf  # the kernel also projects the bias cells it uses
+        ms_two, proj_ms, attn_ms = measure(step_two)
+    else:
+        ms_per_step, proj_ms, attn_ms = measure(step_two)
+        kern_ms = attn_ms
+        kern_fl = fl_layer
+        ms_pair = measure(step_pair)[0] if args.dv == 128 else None
+    kern_avg = float(np.mean(kern_ms))
+    attn_avg = float(np.mean(attn_ms))
+    proj_avg = float(np.mean(proj_ms))
+
+    value = n_layers * fl_layer / (ms_per_step * 1e-3) / 1e12
+    achieved = kern_fl / (kern_avg * 1e-3) / 1e12
+    counters = load_counters(path) if (args.dv == 128 and wl == "full") else None
+    log(f"{path}: step {ms_per_step:.3f} ms; kernel avg {kern_avg * 1e3:.1f} us "
+        f"(median {np.median(kern_ms) * 1e3:.1f}, p95 {np.percentile(kern_ms, 95) * 1e3:.1f}) "
+        f"= {achieved:.1f} TFLOP/s")
+    log(f"two kernels: attention avg {attn_avg * 1e3:.1f} us, projection avg "
+        f"{proj_avg * 1e3:.1f} us = {pb / (proj_avg * 1e-3) / 1e9:.0f} GB/s")
 
     if args.copy_mib > 0:
         n = args.copy_mib << 20
@@ -256,6 +314,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -268,6 +327,8 @@ def main():
                                        "+ biased soft-capped MQA fwd",
                                 "shard": "one GPU's share of full-context layers (queries "
                                          "3072..4095 of 8192, all keys; full projection)"}[wl],
+                   "route": {"pair": "pair form: projection inside the attention kernel",
+                             "two": "projection kernel + attention kernel"}[path],
                    "B": 1, "S": S, "Sq": Sq, "kv_splits": layers[0]["z"], "P": P, "q_heads": 8,
                    "kv_heads": 1, "d": 128, "dv": args.dv,
                    "pair_channels": 128, "layers": n_layers, "softcap": cap,
@@ -278,9 +339,18 @@ def main():
                      "traffic": counters["hbm_bytes_per_launch"] if counters else None,
                      "mfma_flops_counter": counters["mfma_flops_per_launch"] if counters else None,
                      "mfma_busy_frac_counter": counters["mfma_busy_frac"] if counters else None,
-                     "kernel": "biased_mqa_fwd_bf16_capped_kernel",
-                     "avg_launch_us": round(attn_avg * 1e3, 2)},
-        "projection": {"bound": "hbm", "avg_launch_us": round(proj_avg * 1e3, 2),
+                     "kernel": "biased_mqa_fwd_bf16_capped_kernel" +
+                               (" (pair form)" if path == "pair" else ""),
+                     "flops_per_launch": kern_fl,
+                     "avg_launch_us": round(kern_avg * 1e3, 2)},
+        "other_route": ({"route": "projection kernel + attention kernel",
+                         "ms_per_step": round(ms_two, 4),
+                         "attention_avg_launch_us": round(attn_avg * 1e3, 2)}
+                        if path == "pair" else
+                        {"route": "pair form", "ms_per_step": round(ms_pair, 4)}
+                        if ms_pair is not None else None),
+        "projection": {"bound": "hbm", "route": "projection kernel of the two-kernel route",
+                       "avg_launch_us": round(proj_avg * 1e3, 2),
                        "bytes_per_launch": pb,
                        "achieved_GBs": round(pb / (proj_avg * 1e-3) / 1e9, 1),
                        "peak_GBs": PEAK_HBM_GBS,

@@ -258,11 +258,10 @@ __device__ __forceinline__ bf16x2 mask_pair(bf16x2 p, int k, int lim) {
 // Soft-capped weights exp(L - cap) of 16 scores (key cells beta.x for x < 8,
 // beta.y for x >= 8), packed as the PV operand; the row sum adds the packed
 // values.
-template <typename T, bool MASK = false>
+template <typename T>
 __device__ __forceinline__ void softmax_capped(const f32x16& s, f32x2 beta, float alpha,
                                                float den_a, float& rowsum,
-                                               typename Traits<T>::F (&p)[2],
-                                               int lim = 0) {
+                                               typename Traits<T>::F (&p)[2]) {
   float w[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
@@ -280,7 +279,6 @@ __device__ __forceinline__ void softmax_capped(const f32x16& s, f32x2 beta, floa
       for (int m = 0; m < 4; ++m) {
         const f32x2 two = {w[8 * half + 2 * m], w[8 * half + 2 * m + 1]};
         pr[m] = __builtin_convertvector(two, bf16x2);
-        if constexpr (MASK) pr[m] = mask_pair(pr[m], 16 * half + 2 * m, lim);
         rowsum = __builtin_amdgcn_fdot2_f32_bf16(pr[m], ones, rowsum, false);
       }
       bf16x8 f;
@@ -352,22 +350,25 @@ __device__ __forceinline__ void softmax_half(const f32x16& s, f32x2 beta, float 
 // ---------------------------------------------------------------------------
 // Fixed-order stage for bf16 with the cap.
 //
-// Softmax micro-operations of one 32-key half (16 values per lane):
-//   pass 0: t = fma(s, alpha, beta)   1: y = exp2(t)   2: d = fma(y, a, a)
-//   pass 3: r = rcp(d)                4: w = exp2(r)
+// Softmax micro-operations of one 32-key half (16 values per lane).  The
+// scores arrive as exponents t = alpha s + beta (Q pre-scaled by alpha, the
+// accumulator started from beta):
+//   pass 1: y = exp2(t)   2: d = fma(y, a, a)   3: r = rcp(d)   4: w = exp2(r)
 //   pass 5: pack pair k to bf16       6: row sum += the packed pair
-// issued as a skewed pipeline: at step tau, pass p works on value tau - 3p,
-// and pair k is packed two steps after its second value is done.
+// issued as a skewed pipeline: at step tau, pass p works on value
+// tau - 3 (p - 1), and pair k is packed two steps after its second value is
+// done.
 // ---------------------------------------------------------------------------
 struct SmOp { int pass, idx; };
-struct SmTable { SmOp op[96]; };
+constexpr int kSmOps = 80;  // 16 values x 4 passes + 8 packs + 8 sums
+struct SmTable { SmOp op[kSmOps]; };
 constexpr SmTable make_sm_table() {
   SmTable t{};
   int n = 0;
-  constexpr int lag = 3, fe = 4 * lag + 3;
-  for (int tau = 0; n < 96; ++tau) {
-    for (int p = 0; p < 5; ++p) {
-      const int x = tau - p * lag;
+  constexpr int lag = 3, fe = 3 * lag + 3;
+  for (int tau = 0; n < kSmOps; ++tau) {
+    for (int p = 1; p < 5; ++p) {
+      const int x = tau - (p - 1) * lag;
       if (x >= 0 && x < 16) t.op[n++] = SmOp{p, x};
     }
     if (tau >= fe && (tau - fe) % 2 == 0 && (tau - fe) / 2 < 8) t.op[n++] = SmOp{5, (tau - fe) / 2};
@@ -383,11 +384,10 @@ struct SmState {
   bf16x2 pk[8];
 };
 
-__device__ __forceinline__ void sm_op(int pass, int x, SmState& st, const f32x16& s, f32x2 beta,
-                                      float alpha, float den_a, float& rowsum) {
+__device__ __forceinline__ void sm_op(int pass, int x, SmState& st, const f32x16& s, float den_a,
+                                      float& rowsum) {
   switch (pass) {
-    case 0: st.v[x] = __builtin_fmaf(s[x], alpha, x < 8 ? beta.x : beta.y); break;
-    case 1: st.v[x] = __builtin_amdgcn_exp2f(st.v[x]); break;
+    case 1: st.v[x] = __builtin_amdgcn_exp2f(s[x]); break;
     case 2: st.v[x] = __builtin_fmaf(st.v[x], den_a, den_a); break;
     case 3: st.v[x] = __builtin_amdgcn_rcpf(st.v[x]); break;
     case 4: st.v[x] = __builtin_amdgcn_exp2f(st.v[x]); break;
@@ -611,8 +611,14 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
 // ===========================================================================
 // gfx950 path for bf16 inputs with the cap.
 //
-// LDS (bytes): V tiles at s * 16 KiB (s = 0..2), K tiles at 48 KiB + s * 16
-// KiB, bias cells at 96 KiB + s * 256.  Tiles arrive straight from HBM with
+// LDS (bytes, value width 128): V tiles at s * 16 KiB (s = 0..2), K tiles at
+// 48 KiB + s * 16 KiB, bias cells at 96 KiB + s * 256, pair vectors (when the
+// bias is projected in the kernel) at 96.75 KiB + s * 2 KiB, exponent
+// offsets expanded to the accumulator layout at 102.75 KiB + s * 2 KiB.
+// The softmax exponent comes out of the MFMA: Q is scaled by the exponent
+// factor when it is loaded, and each QK^T accumulator starts from the
+// tile's expanded offsets (bias x exponent factor), written one iteration
+// ahead by the wave that reads them.  Tiles arrive straight from HBM with
 // global_load_lds_dwordx4 (16 bytes per lane, no register staging); each lane
 // fetches the chunk that belongs at its LDS slot, which applies the layouts:
 //   * K: LDS row kb*32 + rho holds key kb*32 + key_perm(rho); its 16-byte
@@ -649,7 +655,12 @@ struct FP {
   // query cells x 4 key cells x 128 channels, bf16
   static constexpr int PTILE = 2 * 4 * 128 * 2;
   static constexpr int PR0 = B0 + NBUF * 256;
-  static constexpr int SMEM = PR0 + NBUF * PTILE;
+  // exponent offsets of one tile expanded to the accumulator layout: per head,
+  // half and query cell the 16 values a lane adds to its QK^T accumulator
+  // (8 x key cell 2 half, 8 x key cell 2 half + 1), float
+  static constexpr int XBS = kHeads * 2 * 2 * 16 * 4;
+  static constexpr int XB0 = PR0 + NBUF * PTILE;
+  static constexpr int SMEM = XB0 + NBUF * XBS;
   static_assert(SMEM >= kBlockPos * kHeads * DV * 2, "output staging fits in the tile buffers");
 };
 
@@ -665,15 +676,15 @@ __device__ __forceinline__ constexpr int slot_db(int j) {
 }
 template <int NPV>
 __device__ __forceinline__ constexpr int slot_half(int j) { return j < 8 + NPV ? 0 : 1; }
-// The 96 softmax micro-ops of a stage spread over its slots: as evenly as
+// The softmax micro-ops of a stage spread over its slots: as evenly as
 // possible, the first slots taking one more.
 template <int NSLOT>
 __device__ __forceinline__ constexpr int sm_count(int j) {
-  return 96 / NSLOT + (j < 96 % NSLOT ? 1 : 0);
+  return kSmOps / NSLOT + (j < kSmOps % NSLOT ? 1 : 0);
 }
 template <int NSLOT>
 __device__ __forceinline__ constexpr int sm_begin(int j) {
-  return j * (96 / NSLOT) + (j < 96 % NSLOT ? j : 96 % NSLOT);
+  return j * (kSmOps / NSLOT) + (j < kSmOps % NSLOT ? j : kSmOps % NSLOT);
 }
 
 // V rows in LDS are row-major as in HBM, in 32-byte slots (16 channels)
@@ -714,6 +725,14 @@ __device__ __forceinline__ bf16x8 vfrag(const char* smem, const int (&vro)[DV / 
   return f;
 }
 
+// The expanded offsets of the tile in slot S, half KB, for this lane's query
+// cell: the start of a QK^T accumulator.  xbl[hh] = XB0 + head * 256 +
+// qc * 64 (bytes).
+template <int HPW, int S, int KB, int DV>
+__device__ __forceinline__ f32x16 beta_acc(const char* smem, const int (&xbl)[HPW], int hh) {
+  return *reinterpret_cast<const f32x16*>(smem + xbl[hh] + S * FP<DV>::XBS + KB * 128);
+}
+
 // One stage: for each of the HPW heads of the wave, 16 MFMAs (PV of half KB
 // of the tile in V stage SV, QK^T of half KB of the tile in K stage SK) woven
 // with the softmax of `ssm` into `pout`.  Each A fragment read from LDS feeds
@@ -722,18 +741,17 @@ __device__ __forceinline__ bf16x8 vfrag(const char* smem, const int (&vro)[DV / 
 // stage (PV on half NKB of V stage NSV).
 template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB>
 __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
-                                       const int (&vro)[DV / 32],
+                                       const int (&vro)[DV / 32], const int (&xbl)[HPW],
                                        const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][DV / 32],
                                        f32x16 (&sout)[HPW], const bf16x8 (&pin)[HPW][2],
-                                       const f32x16 (&ssm)[HPW], const f32x2 (&beta)[HPW],
-                                       float alpha, float den_a, float (&rowsum)[HPW],
+                                       const f32x16 (&ssm)[HPW], float den_a, float (&rowsum)[HPW],
                                        bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4]) {
   constexpr int NPV = DV / 32;
   constexpr int NSLOT = 8 + 2 * NPV;
   SmState sm[HPW];
-  f32x16 acc[HPW];
+  f32x16 acc[HPW];  // QK^T of the next half starts from its exponent offsets
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) acc[hh] = f32x16{};
+  for (int hh = 0; hh < HPW; ++hh) acc[hh] = beta_acc<HPW, SK, KB, DV>(smem, xbl, hh);
 #pragma unroll
   for (int j = 0; j < NSLOT; ++j) {
     const int jn = j + 3;
@@ -753,7 +771,7 @@ __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
 #pragma unroll
       for (int u = 0; u < sm_count<NSLOT>(j); ++u)
         sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh],
-              ssm[hh], beta[hh], alpha, den_a, rowsum[hh]);
+              ssm[hh], den_a, rowsum[hh]);
     }
     // inside the slot: the MFMA first, then the LDS reads, then the VALU work
 #pragma unroll
@@ -839,8 +857,10 @@ struct FastCtx {
 
 // Direct HBM -> LDS copy of K and V of tile t into stage S (LPW_K + LPW_V
 // loads per lane, 1 KiB per wave each) and of the tile's bias cells.
+// Direct HBM -> LDS copy of K and V of tile t into stage S (LPW_K + LPW_V
+// loads per lane, 1 KiB per wave each).
 template <int HPW, int DV, bool TAIL, bool FUSED, int S>
-__device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV, FUSED>& c, int t) {
+__device__ __forceinline__ void issue_kv(char* smem, const FastCtx<HPW, DV, FUSED>& c, int t) {
   using L = FP<DV>;
   using Ctx = FastCtx<HPW, DV, FUSED>;
   const char* kt = c.kb_ptr + (int64_t)t * L::KTILE;
@@ -858,15 +878,22 @@ __device__ __forceinline__ void issue_tile(char* smem, const FastCtx<HPW, DV, FU
   for (int j = 0; j < Ctx::LPW_V; ++j)
     lds_copy16(vt, TAIL ? min(c.goff_v[j], vcap) : c.goff_v[j],
                lds + L::V0 + S * L::VTILE + (uint32_t)((Ctx::LPW_V * c.wave + j) * 1024));
+}
+
+// Direct copy of what tile t's exponent offsets are made from into slot S:
+// its 64 compact-bias cells (8 heads x 2 query cells x 4 key cells, one per
+// lane of wave 0), or with FUSED its 8 pair vectors (2 query cells x 4 key
+// cells, 1 KiB per query cell, waves 0 and 1).  Cells past the last one are
+// clamped to it.
+template <int HPW, int DV, bool TAIL, bool FUSED, int S>
+__device__ __forceinline__ void issue_cells(char* smem, const FastCtx<HPW, DV, FUSED>& c, int t) {
+  using L = FP<DV>;
+  const uint32_t lds = (uint32_t)(size_t)(lds_void*)smem;
   if constexpr (FUSED) {
-    // the tile's 8 pair vectors (2 query cells x 4 key cells, 1 KiB per
-    // query cell), projected by each wave for its heads once they arrive
     if (c.wave < 2)
       lds_copy16(c.pr_base, min(c.pr_cell + 4 * t, c.pm1) * 256 + (int)(threadIdx.x & 15) * 16,
                  lds + L::PR0 + S * L::PTILE + c.wave * 1024);
   } else {
-    // the tile's 64 compact-bias cells (8 heads x 2 query blocks x 4 key
-    // blocks), one per lane of wave 0
     if (c.wave == 0)
       lds_copy4(c.bias_lane + (TAIL ? min(4 * t, c.bias_cap) : 4 * t), lds + L::B0 + S * 256);
   }
@@ -889,14 +916,34 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-// Compact-bias cells projected in the kernel.  For the tile in stage S,
-// cell (query cell qc, key cell kc) of head h is sum_c pair[qc, kc, c] W[c, h]
-// (bf16 products, float32 sums).  Lane l holds channels 16 (l & 7) .. + 15
-// of pair vector l >> 3 = 4 qc + kc (pair_load); the 8 lanes of a vector sum
-// it and all store the (identical) sum where the copied bias would be
-// (pair_store) -- no branch, which would split the stage's schedule.  Each
-// wave writes, and later reads, only its own heads' cells, so the in-order
+// Exponent offsets of the tile in slot S for the wave's heads: beta = bias
+// cell x the exponent factor, written expanded to the accumulator layout of
+// the QK^T product (XB0: per head, half hf and query cell qc, 8 copies of key
+// cell 2 hf and 8 of key cell 2 hf + 1), so that a QK^T accumulator starts
+// from them with four broadcast LDS reads and the softmax needs no add.  A
+// wave writes, and later reads, only its own heads' offsets, so the in-order
 // LDS accesses of the wave suffice: no barrier.
+//
+// From copied compact-bias cells: lane l writes entry l of the head's 64
+// (hf = l >> 5, qc = (l >> 4) & 1, key cell 2 hf + ((l >> 3) & 1)).
+template <int HPW, int DV, int S>
+__device__ __forceinline__ void expand_bias(char* smem, int wave, float beta_mul) {
+  using L = FP<DV>;
+  const int lane = (int)threadIdx.x & 63;
+  const int cell = ((lane >> 4) & 1) * 4 + 2 * (lane >> 5) + ((lane >> 3) & 1);
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = wave * HPW + hh;
+    const float b = reinterpret_cast<const float*>(smem + L::B0 + S * 256)[h * 8 + cell];
+    reinterpret_cast<float*>(smem + L::XB0 + S * L::XBS)[h * 64 + lane] = b * beta_mul;
+  }
+}
+
+// Projected from the pair vectors (FUSED).  Cell (qc, kc) of head h is
+// sum_c pair[qc, kc, c] W[c, h] (bf16 products, float32 sums).  Lane l holds
+// channels 16 (l & 7) .. + 15 of pair vector l >> 3 = 4 qc + kc (pair_load);
+// the 8 lanes of a vector sum it, and lane l & 7 writes copy l & 7 of the
+// cell's 8 (pair_store).
 template <int DV, int S>
 __device__ __forceinline__ void pair_load(const char* smem, bf16x8 (&a)[2]) {
   using L = FP<DV>;
@@ -907,9 +954,11 @@ __device__ __forceinline__ void pair_load(const char* smem, bf16x8 (&a)[2]) {
 }
 template <int HPW, int DV, int S>
 __device__ __forceinline__ void pair_store(char* smem, const bf16x8 (&a)[2], const uint32_t (&wreg)[HPW][8],
-                                           int wave) {
+                                           int wave, float beta_mul) {
   using L = FP<DV>;
   const int lane = (int)threadIdx.x & 63;
+  const int v = lane >> 3, qc = v >> 2, kc = v & 3;
+  const int entry = (kc >> 1) * 32 + qc * 16 + (kc & 1) * 8 + (lane & 7);
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     float s[2] = {0.f, 0.f};  // two chains, added at the end
@@ -919,51 +968,73 @@ __device__ __forceinline__ void pair_store(char* smem, const bf16x8 (&a)[2], con
       const bf16x2 x = {a[i >> 2][2 * (i & 3)], a[i >> 2][2 * (i & 3) + 1]};
       s[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(x, w, s[i & 1], false);
     }
-    const float t = sum8(s[0] + s[1]);
-    reinterpret_cast<float*>(smem + L::B0 + S * 256)[(wave * HPW + hh) * 8 + (lane >> 3)] = t;
+    const float t = sum8(s[0] + s[1]) * beta_mul;
+    reinterpret_cast<float*>(smem + L::XB0 + S * L::XBS)[(wave * HPW + hh) * 64 + entry] = t;
   }
-}
-
-template <int HPW, int S>
-__device__ __forceinline__ void read_beta(const char* smem, const int (&bias_l)[HPW], int half,
-                                          float beta_mul, f32x2 (&beta)[HPW]) {
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-    beta[hh] = *reinterpret_cast<const f32x2*>(smem + bias_l[hh] + S * 256 + 8 * half) * beta_mul;
 }
 
 // One pipelined iteration for tile t in stage C.
 template <int HPW, int DV, bool TAIL, bool FUSED, int C>
 __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUSED>& c, int t, int last,
                                           const int (&kro)[8], const int (&vro)[DV / 32],
-                                          const int (&bias_l)[HPW], const bf16x8 (&qf)[HPW][8],
+                                          const int (&xbl)[HPW], const bf16x8 (&qf)[HPW][8],
                                           f32x16 (&O)[HPW][DV / 32], f32x16 (&S0)[HPW],
                                           f32x16 (&S1)[HPW], bf16x8 (&P0)[HPW][2],
-                                          bf16x8 (&P1)[HPW][2], float alpha,
+                                          bf16x8 (&P1)[HPW][2],
                                           float den_a, float (&rowsum)[HPW], bf16x8 (&ring)[4]) {
   constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
-  // tile t+2 into the stage that held tile t-1 (clamped past the end: the
-  // copy lands in a stage nobody reads again)
-  issue_tile<HPW, DV, TAIL, FUSED, NN>(smem, c, min(t + 2, last));
+  // K and V of tile t+2 into the stage that held tile t-1, and the cells of
+  // tile t+3 into the slot that held tile t's (expanded two iterations ago);
+  // past the end the copies are clamped and land where nobody reads again
+  issue_kv<HPW, DV, TAIL, FUSED, NN>(smem, c, min(t + 2, last));
+  issue_cells<HPW, DV, TAIL, FUSED, C>(smem, c, min(t + 3, last));
   bf16x8 pv[2];
-  if constexpr (FUSED) pair_load<DV, NXT>(smem, pv);  // pair vectors of tile t+1, read during X
-  f32x2 beta[HPW];
+  if constexpr (FUSED) pair_load<DV, NN>(smem, pv);  // pair vectors of tile t+2, read during X
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
-  read_beta<HPW, C>(smem, bias_l, 1, c.beta_mul, beta);
-  fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, qf, O, S0, P0, S1, beta, alpha, den_a, rowsum, P1, ring);
+  fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, P1, ring);
+  // the exponent offsets of tile t+2, read by the next iteration
+  if constexpr (FUSED) pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
+  else expand_bias<HPW, DV, NN>(smem, c.wave, c.beta_mul);
   // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
-  if constexpr (FUSED) pair_store<HPW, DV, NXT>(smem, pv, c.wreg, c.wave);  // bias cells of tile t+1
-  read_beta<HPW, NXT>(smem, bias_l, 0, c.beta_mul, beta);
-  fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, qf, O, S1, P1, S0, beta, alpha, den_a, rowsum, P0, ring);
+  fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, P0, ring);
   tile_barrier();
+}
+
+// Soft-capped weights exp(L - cap) of 16 exponents t (t = alpha s + beta
+// from the accumulator), packed as the PV operand; the row sum adds the
+// packed values.  MASK: keys past the end of the sequence get p = 0.
+template <bool MASK>
+__device__ __forceinline__ void softmax_exp(const f32x16& t, float den_a, float& rowsum, bf16x8 (&p)[2],
+                                            int lim) {
+  float w[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const float y = __builtin_amdgcn_exp2f(t[x]);
+    const float d = __builtin_fmaf(y, den_a, den_a);
+    w[x] = __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(d));
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    bf16x2 pr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x2 two = {w[8 * half + 2 * m], w[8 * half + 2 * m + 1]};
+      pr[m] = __builtin_convertvector(two, bf16x2);
+      if constexpr (MASK) pr[m] = mask_pair(pr[m], 16 * half + 2 * m, lim);
+      rowsum = __builtin_amdgcn_fdot2_f32_bf16(pr[m], ones, rowsum, false);
+    }
+    bf16x8 f;
+    __builtin_memcpy(&f, pr, 16);
+    p[half] = f;
+  }
 }
 
 // Last tile (stage C): PV of both halves and the softmax of its second half.
 template <int HPW, int DV, bool TAIL, int C>
 __device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, const int (&vro)[DV / 32],
-                                          const int (&bias_l)[HPW], f32x16 (&O)[HPW][DV / 32],
-                                          const f32x16 (&S1)[HPW], const bf16x8 (&P0)[HPW][2],
-                                          float alpha, float beta_mul, float den_a,
+                                          f32x16 (&O)[HPW][DV / 32], const f32x16 (&S1)[HPW],
+                                          const bf16x8 (&P0)[HPW][2], float den_a,
                                           float (&rowsum)[HPW]) {
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
@@ -973,13 +1044,10 @@ __device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, cons
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P0[hh][half]);
     }
-  f32x2 beta[HPW];
-  read_beta<HPW, C>(smem, bias_l, 1, beta_mul, beta);
   bf16x8 P1[HPW][2];
   const int lim = klim_half1 - 8 * lane_g();
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-    softmax_capped<__bf16, TAIL>(S1[hh], beta[hh], alpha, den_a, rowsum[hh], P1[hh], lim);
+  for (int hh = 0; hh < HPW; ++hh) softmax_exp<TAIL>(S1[hh], den_a, rowsum[hh], P1[hh], lim);
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -990,15 +1058,19 @@ __device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, cons
     }
 }
 
-// B operand of QK^T: lane (r, g) holds dk 16 kc + 8 g .. + 7 of its query
-// row, for the HPW heads that follow `qrow`.
+// B operand of QK^T, pre-scaled: lane (r, g) holds alpha x dk 16 kc + 8 g ..
+// + 7 of its query row (rounded to bf16), for the HPW heads that follow
+// `qrow`.  With the accumulator started from beta, the product is then the
+// softmax exponent itself.
 template <int HPW>
-__device__ __forceinline__ void load_q(const __bf16* qrow, int g, bf16x8 (&qf)[HPW][kD / 16]) {
+__device__ __forceinline__ void load_q(const __bf16* qrow, int g, float alpha, bf16x8 (&qf)[HPW][kD / 16]) {
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int kc = 0; kc < kD / 16; ++kc)
-      qf[hh][kc] = *reinterpret_cast<const bf16x8*>(qrow + hh * kD + kc * 16 + 8 * g);
+    for (int kc = 0; kc < kD / 16; ++kc) {
+      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(qrow + hh * kD + kc * 16 + 8 * g);
+      qf[hh][kc] = __builtin_convertvector(__builtin_convertvector(raw, f32x8) * alpha, bf16x8);
+    }
 }
 // LDS offsets of the K^T A operand (key row r, XOR-swizzled 16-byte chunks).
 template <int DV>
@@ -1014,12 +1086,12 @@ __device__ __forceinline__ void k_read_offsets(int r, int g, int (&kro)[8]) {
 // qpos0 of this workgroup (rows past Sq read row Sq - 1).  Q and the K
 // offsets are loaded again here rather than kept from the start: holding
 // them past the pipelined loop costs more registers than that loop leaves.
-template <int HPW, int DV, bool FUSED, int C>
-__device__ __forceinline__ void fast_partial(const FastCtx<HPW, DV, FUSED>& c, int lim0, const __bf16* qb,
-                                             int qpos0, int Sq, char* smem,
-                                             const int (&vro)[DV / 32], const int (&bias_l)[HPW],
-                                             f32x16 (&O)[HPW][DV / 32], float alpha, float beta_mul,
-                                             float den_a, float (&rowsum)[HPW]) {
+// The tile's exponent offsets were expanded two iterations before.
+template <int HPW, int DV, int C>
+__device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpos0, int Sq, const char* smem,
+                                             const int (&vro)[DV / 32], const int (&xbl)[HPW],
+                                             f32x16 (&O)[HPW][DV / 32], float alpha, float den_a,
+                                             float (&rowsum)[HPW]) {
   // opaque to the compiler, so that it reloads instead of reusing the values
   // read before the loop
   int lane = (int)threadIdx.x & 63;
@@ -1027,35 +1099,31 @@ __device__ __forceinline__ void fast_partial(const FastCtx<HPW, DV, FUSED>& c, i
   const int g = lane >> 5;
   const __bf16* qrow = qb + (int64_t)(min(qpos0 + (lane & 31), Sq - 1) - qpos0) * kHeads * kD;
   bf16x8 qf[HPW][kD / 16];
-  load_q<HPW>(qrow, g, qf);
+  load_q<HPW>(qrow, g, alpha, qf);
   int kro[8];
   k_read_offsets<DV>(lane & 31, g, kro);
   const int lim = lim0 - 8 * g;
-  if constexpr (FUSED) {  // bias cells of this tile
-    bf16x8 pv[2];
-    pair_load<DV, C>(smem, pv);
-    pair_store<HPW, DV, C>(smem, pv, c.wreg, c.wave);
-  }
   // QK of both halves first, so that Q and the K offsets are dead before
   // the value fragments are read
   f32x16 sc[2][HPW];
 #pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    sc[0][hh] = beta_acc<HPW, C, 0, DV>(smem, xbl, hh);
+    sc[1][hh] = beta_acc<HPW, C, 1, DV>(smem, xbl, hh);
+  }
+#pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      sc[kb][hh] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) mfma(sc[kb][hh], kfrag<DV, C>(smem, kro, kb, kc), qf[hh][kc]);
     }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     __builtin_amdgcn_sched_barrier(0);
-    f32x2 beta[HPW];
-    read_beta<HPW, C>(smem, bias_l, kb, beta_mul, beta);
     bf16x8 P[HPW][2];
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-      softmax_capped<__bf16, true>(sc[kb][hh], beta[hh], alpha, den_a, rowsum[hh], P[hh], lim - 32 * kb);
+    for (int hh = 0; hh < HPW; ++hh) softmax_exp<true>(sc[kb][hh], den_a, rowsum[hh], P[hh], lim - 32 * kb);
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -1159,15 +1227,15 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     for (int db = 0; db < NPV; ++db)
       vro[db] = L::V0 + row * L::VROW + v_physical_slot<DV>(2 * db + (grp & 1), row) * 32 + 8 * (i16 & 3);
   }
-  int bias_l[HPW];
+  int xbl[HPW];  // this lane's expanded exponent offsets: head, query cell r >> 4
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) bias_l[hh] = L::B0 + ((w * HPW + hh) * 8 + (r >> 4) * 4) * 4;
+  for (int hh = 0; hh < HPW; ++hh) xbl[hh] = L::XB0 + (w * HPW + hh) * 256 + (r >> 4) * 64;
 
   // the wave's first head in the block's first query row, and in this
   // lane's row (rows past Sq read row Sq - 1)
   const __bf16* qb = q + (((int64_t)b * Sq + qpos0) * kHeads + c.wave * HPW) * kD;
   bf16x8 qf[HPW][kD / 16];
-  load_q<HPW>(qb + (int64_t)((TAIL ? min(qpos0 + r, Sq - 1) : qpos0 + r) - qpos0) * kHeads * kD, g, qf);
+  load_q<HPW>(qb + (int64_t)((TAIL ? min(qpos0 + r, Sq - 1) : qpos0 + r) - qpos0) * kHeads * kD, g, alpha, qf);
 
   f32x16 O[HPW][NPV];
   float rowsum[HPW];
@@ -1178,30 +1246,42 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     for (int db = 0; db < NPV; ++db) O[hh][db] = f32x16{};
   }
 
-  // ---- prologue: tiles 0 and 1 -------------------------------------------------
-  issue_tile<HPW, DV, TAIL, FUSED, 0>(smem, c, 0);
-  issue_tile<HPW, DV, TAIL, FUSED, 1>(smem, c, min(1, last));
+  // ---- prologue: K/V of tiles 0 and 1, cells of tiles 0..2 ---------------------
+  issue_kv<HPW, DV, TAIL, FUSED, 0>(smem, c, 0);
+  issue_kv<HPW, DV, TAIL, FUSED, 1>(smem, c, min(1, last));
+  issue_cells<HPW, DV, TAIL, FUSED, 0>(smem, c, 0);
+  issue_cells<HPW, DV, TAIL, FUSED, 1>(smem, c, min(1, last));
+  issue_cells<HPW, DV, TAIL, FUSED, 2>(smem, c, min(2, last));
   tile_barrier();
-  if constexpr (FUSED) {  // bias cells of tile 0
+  // exponent offsets of tiles 0 and 1 (iteration t expands tile t+2)
+  if constexpr (FUSED) {
     bf16x8 pv[2];
     pair_load<DV, 0>(smem, pv);
-    pair_store<HPW, DV, 0>(smem, pv, c.wreg, c.wave);
+    pair_store<HPW, DV, 0>(smem, pv, c.wreg, c.wave, beta_mul);
+    pair_load<DV, 1>(smem, pv);
+    pair_store<HPW, DV, 1>(smem, pv, c.wreg, c.wave, beta_mul);
+  } else {
+    expand_bias<HPW, DV, 0>(smem, c.wave, beta_mul);
+    expand_bias<HPW, DV, 1>(smem, c.wave, beta_mul);
   }
 
   f32x16 S0[HPW], S1[HPW];
   bf16x8 P0[HPW][2], P1[HPW][2];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    S0[hh] = f32x16{};
-    S1[hh] = f32x16{};
+    S0[hh] = beta_acc<HPW, 0, 0, DV>(smem, xbl, hh);
+    S1[hh] = beta_acc<HPW, 0, 1, DV>(smem, xbl, hh);
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       mfma(S0[hh], kfrag<DV, 0>(smem, kro, 0, kc), qf[hh][kc]);
       mfma(S1[hh], kfrag<DV, 0>(smem, kro, 1, kc), qf[hh][kc]);
     }
-    softmax_capped<__bf16, TAIL>(S0[hh], *reinterpret_cast<const f32x2*>(smem + bias_l[hh]) * beta_mul,
-                                 alpha, den_a, rowsum[hh], P0[hh], klim - 8 * g);
+    softmax_exp<TAIL>(S0[hh], den_a, rowsum[hh], P0[hh], klim - 8 * g);
   }
+  // iteration 0 copies tile 3's cells into slot 0, which other waves may
+  // still be reading for tile 0 above (later slots are two barriers past
+  // their last read when they are overwritten)
+  __syncthreads();
   bf16x8 ring[4];
 #pragma unroll
   for (int j = 0; j < 3; ++j) ring[j] = vfrag<DV, 0>(smem, vro, j, 0);
@@ -1215,26 +1295,26 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   int t = 0;
   while (true) {
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, FUSED, 0>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, 0>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum, ring);
     ++t;
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, FUSED, 1>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, 1>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum, ring);
     ++t;
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, FUSED, 2>(smem, c, t, last, kro, vro, bias_l, qf, O, S0, S1, P0, P1, alpha, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, 2>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum, ring);
     ++t;
   }
   switch (lastp % 3) {
-    case 0: fast_tail<HPW, DV, TAIL, 0>(klim - 64 * lastp - 32, smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
-    case 1: fast_tail<HPW, DV, TAIL, 1>(klim - 64 * lastp - 32, smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
-    default: fast_tail<HPW, DV, TAIL, 2>(klim - 64 * lastp - 32, smem, vro, bias_l, O, S1, P0, alpha, beta_mul, den_a, rowsum); break;
+    case 0: fast_tail<HPW, DV, TAIL, 0>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum); break;
+    case 1: fast_tail<HPW, DV, TAIL, 1>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum); break;
+    default: fast_tail<HPW, DV, TAIL, 2>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum); break;
   }
   if constexpr (TAIL) {
-    if (c.tile_end > 0) {  // uniform; the tile was loaded by the last iteration or the prologue
+    if (c.tile_end > 0) {  // uniform; the tile was loaded and its offsets expanded before
       switch (last % 3) {
-        case 0: fast_partial<HPW, DV, FUSED, 0>(c, klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
-        case 1: fast_partial<HPW, DV, FUSED, 1>(c, klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
-        default: fast_partial<HPW, DV, FUSED, 2>(c, klim - 64 * last, qb, qpos0, Sq, smem, vro, bias_l, O, alpha, beta_mul, den_a, rowsum); break;
+        case 0: fast_partial<HPW, DV, 0>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum); break;
+        case 1: fast_partial<HPW, DV, 1>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum); break;
+        default: fast_partial<HPW, DV, 2>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum); break;
       }
     }
   }

@@ -300,6 +300,22 @@ def test_attention_tails(case):
     print(f"  tails {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
 
 
+def test_attention_long_sampled():
+    """S = 65536 (4096 compact cells per side, 1024 key tiles, a 512 MiB
+    bias), far past the workloads' lengths: sampled rows, through the
+    plain call and with key ranges."""
+    L = workloads.make_custom(B=1, S=65536, dtype="bf16", C=8, seed=65536, qkv_std=1.0, bias_std=2.0)
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    one = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, scale=L.scale, softcap=L.cap)
+    split = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, scale=L.scale, softcap=L.cap, kv_splits=4)
+    torch.cuda.synchronize()
+    bias64 = _oracle_bias(L)
+    rows = sample_rows(L.S, seed=5)
+    _check_rows(L, to_host(one), bias64, rows)
+    _check_rows(L, to_host(split), bias64, rows)
+
+
 def test_single_key_returns_its_value():
     """S = 1: every query attends to the one key with weight 1, so the output
     is that key's value row (rounded to bf16 it is exact)."""

@@ -94,6 +94,23 @@ def load_counters(path):
         return None
 
 
+def environment(torch, dev):
+    """Versions and device figures recorded with each result."""
+    p = torch.cuda.get_device_properties(dev)
+    env = {"device": p.name, "gcn_arch": getattr(p, "gcnArchName", None),
+           "compute_units": p.multi_processor_count, "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None)}
+    clk = getattr(p, "clock_rate", None)
+    if clk:
+        env["max_clock_mhz"] = round(clk / 1000.0)
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    return env
+
+
 def cpu_baseline(host_layers):
     """The oracle (unchanged) on a bounded sample of the workload: the first
     layers (projection + all 8192 x 8 output rows each), timed on this host's
@@ -342,7 +359,9 @@ def main():
                      "kernel": "biased_mqa_fwd_bf16_capped_kernel" +
                                (" (pair form)" if path == "pair" else ""),
                      "flops_per_launch": kern_fl,
-                     "avg_launch_us": round(kern_avg * 1e3, 2)},
+                     "avg_launch_us": round(kern_avg * 1e3, 2),
+                     "median_launch_us": round(float(np.median(kern_ms)) * 1e3, 2),
+                     "p95_launch_us": round(float(np.percentile(kern_ms, 95)) * 1e3, 2)},
         "other_route": ({"route": "projection kernel + attention kernel",
                          "ms_per_step": round(ms_two, 4),
                          "attention_avg_launch_us": round(attn_avg * 1e3, 2)}
@@ -356,6 +375,7 @@ def main():
                        "peak_GBs": PEAK_HBM_GBS,
                        "frac": round(pb / (proj_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": cpu,
+        "env": environment(torch, dev),
     }
     print(json.dumps(rec), flush=True)
 

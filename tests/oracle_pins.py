@@ -61,8 +61,13 @@ def _close(a, b, tol):
 # Brute force on tiny shapes
 # --------------------------------------------------------------------------
 def pin_brute_force(attn):
+    # lengths off the 16-position cell (7, 23, 40) pin a last cell that is
+    # shorter than 16 positions: the brute force indexes the compact bias by
+    # integer division and never builds the repeated bias
     for seed, (S, Hq, D, cap) in enumerate([(16, 1, 4, CAP), (32, 2, 4, CAP),
-                                            (48, 8, 4, 1.5), (32, 3, 8, 0.0)]):
+                                            (48, 8, 4, 1.5), (32, 3, 8, 0.0),
+                                            (7, 2, 4, CAP), (23, 1, 4, CAP),
+                                            (40, 2, 4, 1.5)]):
         q, k, v, bias = _rand_case(100 + seed, B=2, S=S, Hq=Hq, Dk=D, Dv=D + 1,
                                    qkv_std=1.5, bias_std=2.0)
         scale = 1.0 / math.sqrt(D)

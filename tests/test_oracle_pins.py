@@ -49,6 +49,12 @@ def test_attention_rows_matches_full():
     rows = np.array([0, 15, 16, 63, 64, 127])
     part = oracle.attention_rows(q, k, v, bias, rows, scale=0.25, cap=5.0, batch=1)
     assert np.allclose(part, full[1, rows], rtol=0, atol=1e-15)
+    # a length off the 16-position cell (P = ceil(S/16)), against the brute force
+    q, k, v, bias = pins._rand_case(601, B=1, S=37, Hq=2, Dk=4, Dv=4, bias_std=2.0)
+    rows = np.array([0, 15, 16, 31, 32, 36])
+    part = oracle.attention_rows(q, k, v, bias, rows, scale=0.5, cap=5.0, batch=0)
+    brute = np.array(oracle.attention_brute(q, k, v, bias, scale=0.5, cap=5.0))[0, rows]
+    assert np.allclose(part, brute, rtol=0, atol=1e-12)
 
 
 def test_bf16_decoding_is_exact():

@@ -490,9 +490,52 @@ def test_deterministic_and_stream_ordered():
         assert torch.equal(o, ref)
 
 
+def test_graph_capture_replays():
+    """The calls capture into a HIP graph (through torch.cuda.graph) and every
+    replay equals the eager result bit for bit: the plain call, key ranges
+    with a caller-owned workspace, and the pair form.  Eager work runs
+    between the replays, and each replay is checked on its own."""
+    L = workloads.make_custom(B=1, S=1000, dtype="bf16", C=128, seed=77, qkv_std=1.0, bias_std=2.0)
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    ws = torch.empty(abg_workspace_bytes(1, 1000, 8, 128, 4), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(t["q"]) for _ in range(3)]
+
+    def calls():
+        biased_mqa_fwd(t["q"], t["k"], t["v"], bias, outs[0], scale=L.scale, softcap=L.cap)
+        biased_mqa_fwd(t["q"], t["k"], t["v"], bias, outs[1], scale=L.scale, softcap=L.cap,
+                       kv_splits=4, workspace=ws)
+        pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], outs[2],
+                            scale=L.scale, softcap=L.cap)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the capture stream
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        # eager work between the replays, on other buffers
+        biased_mqa_fwd(t["q"], t["k"], t["v"], bias, scale=L.scale, softcap=L.cap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, r), f"replay {rep}, call {i}"
+
+
 def test_library_allocates_nothing():
     """Only the caller's tensors exist: the library allocates no device memory
-    (no dense logits, no dense bias)."""
+    (no dense logits, no dense bias; the pair form not even the compact
+    bias)."""
     L = workloads.make_layer("full", layer=2)
     t = upload(L)
     bias = torch.empty((8, L.S // 16, L.S // 16), dtype=torch.float32, device="cuda")
@@ -503,6 +546,7 @@ def test_library_allocates_nothing():
     free_before, _ = torch.cuda.mem_get_info()
     pair_bias_project(t["pair"], t["weight"], out=bias)
     biased_mqa_fwd(t["q"], t["k"], t["v"], bias, out=out)
+    pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], out)  # no bias at all
     torch.cuda.synchronize()
     free_after, _ = torch.cuda.mem_get_info()
     assert torch.cuda.max_memory_allocated() == before

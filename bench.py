@@ -65,11 +65,17 @@ def proj_flops(P, C, H=8):
 
 
 def source_digest():
+    """First 16 hex digits of the sha256 of the attention kernel's source and
+    its launch header with // comments and runs of white space removed: an
+    edit of the comments keeps counters taken on the kernel, any change of
+    the code drops them."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("biased_mqa_fwd.hip", "abg_internal.h"):
-        with open(os.path.join(ROOT, "long_context_biased_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "long_context_biased_amd", "csrc", f)) as fh:
+            code = re.sub(r"//[^\n]*", "", fh.read())
+        h.update(re.sub(r"\s+", " ", code).encode())
     return h.hexdigest()[:16]
 
 

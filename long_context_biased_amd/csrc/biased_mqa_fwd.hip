@@ -39,7 +39,7 @@
 //     matrix cores and the VALU work at the same time inside one wave; the
 //     second wave on the SIMD fills the remaining gaps.  For bf16 with the
 //     cap the order is fixed by hand: 16 slots of {LDS read three MFMAs
-//     ahead, one MFMA, six softmax micro-ops}, the softmax written as a
+//     ahead, one MFMA, five softmax micro-ops}, the softmax written as a
 //     skewed pipeline over its 16 values so dependent operations are far
 //     apart;
 //   * LDS tiles are triple-buffered for bf16 (one barrier per tile) and
@@ -733,12 +733,13 @@ __device__ __forceinline__ f32x16 beta_acc(const char* smem, const int (&xbl)[HP
   return *reinterpret_cast<const f32x16*>(smem + xbl[hh] + S * FP<DV>::XBS + KB * 128);
 }
 
-// One stage: for each of the HPW heads of the wave, 16 MFMAs (PV of half KB
-// of the tile in V stage SV, QK^T of half KB of the tile in K stage SK) woven
-// with the softmax of `ssm` into `pout`.  Each A fragment read from LDS feeds
-// the MFMAs of all HPW heads.  ring[] holds A fragments three slots ahead;
-// the last three slots fetch the first three fragments of the following
-// stage (PV on half NKB of V stage NSV).
+// One stage: for each of the HPW heads of the wave, 8 + 2 DV/32 MFMAs (PV of
+// half KB of the tile in V stage SV, QK^T of half KB of the tile in K stage
+// SK, its accumulator started from that half's exponent offsets) woven with
+// the softmax of the exponents `ssm` into `pout`.  Each A fragment read from
+// LDS feeds the MFMAs of all HPW heads.  ring[] holds A fragments three
+// slots ahead; the last three slots fetch the first three fragments of the
+// following stage (PV on half NKB of V stage NSV).
 template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB>
 __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
                                        const int (&vro)[DV / 32], const int (&xbl)[HPW],
@@ -855,8 +856,6 @@ struct FastCtx {
   float beta_mul;       // factor of the bias in the exp2 argument
 };
 
-// Direct HBM -> LDS copy of K and V of tile t into stage S (LPW_K + LPW_V
-// loads per lane, 1 KiB per wave each) and of the tile's bias cells.
 // Direct HBM -> LDS copy of K and V of tile t into stage S (LPW_K + LPW_V
 // loads per lane, 1 KiB per wave each).
 template <int HPW, int DV, bool TAIL, bool FUSED, int S>

@@ -6,7 +6,7 @@ transformer block), each = pair-bias projection ([512,512,128] bf16 ->
 8 query heads, 1 K/V head, d=128, bf16 inputs, fp32 accumulation), back to
 back on one stream with every input already resident in HBM.
 
-Two routes compute a layer: the pair form (default for d_v = 128), one
+Two routes compute a layer: the pair form (the default), one
 kernel that projects the bias cells it uses inside the attention and never
 writes a bias tensor; and two kernels, the projection writing the compact
 fp32 bias and the attention reading it.  The route not timed is measured
@@ -165,8 +165,8 @@ def main():
                          "the clock takes tens of ms of sustained load to settle, and a route "
                          "timed while it still moves reads up to 30%% slow")
     ap.add_argument("--path", default=None, choices=("pair", "two"),
-                    help="pair: the projection inside the attention kernel (default for dv "
-                         "128); two: projection kernel + attention kernel (default for dv 192)")
+                    help="pair (default): the projection inside the attention kernel; two: "
+                         "projection kernel + attention kernel")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 3 plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -176,10 +176,7 @@ def main():
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
-    path = args.path or ("pair" if args.dv == 128 else "two")
-    if path == "pair" and args.dv != 128:
-        print("the pair form is implemented for dv 128 only", file=sys.stderr)
-        sys.exit(2)
+    path = args.path or "pair"
 
     import torch
     from long_context_biased_amd import (biased_mqa_fwd, pair_bias_project, pair_biased_mqa_fwd,
@@ -295,7 +292,7 @@ def main():
         ms_per_step, proj_ms, attn_ms = measure(step_two)
         kern_ms = attn_ms
         kern_fl = fl_layer
-        ms_pair = measure(step_pair)[0] if args.dv == 128 else None
+        ms_pair = measure(step_pair)[0]
     kern_avg = float(np.mean(kern_ms))
     attn_avg = float(np.mean(attn_ms))
     proj_avg = float(np.mean(proj_ms))

@@ -186,7 +186,7 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
  *   weight  [C, Hq]       bf16
  *
  * Limits beyond abg_biased_mqa_fwd_ex's: dtype ABG_BF16 with softcap > 0;
- * Dv == 128; C == 128; pair_batch_stride 0 or >= P*P*C and a multiple of 8;
+ * Dv == 128 or 192; C == 128; pair_batch_stride 0 or >= P*P*C and a multiple of 8;
  * 1 <= pair_group <= B; pair and weight 16-byte aligned and not overlapping
  * out or the workspace.  kv_splits, q_offset and the workspace work as for
  * abg_biased_mqa_fwd_ex. */

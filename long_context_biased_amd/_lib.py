@@ -258,7 +258,7 @@ def pair_biased_mqa_fwd(q, k, v, pair, weight, out=None, *, scale: Optional[floa
     from ``pair`` [P, P, 128] or [Bp, P, P, 128] and ``weight`` [128, 8] (both
     bfloat16; P = ceil(Sk/16)), so that no bias tensor is ever written.  Item
     b reads pair block b // pair_group.  bfloat16 inputs with the cap, value
-    width 128.  Returns ``out`` [B, Sq, 8, 128].
+    width 128 or 192.  Returns ``out`` [B, Sq, 8, Dv].
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (pair, "pair"), (weight, "weight")):

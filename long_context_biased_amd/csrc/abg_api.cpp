@@ -106,9 +106,8 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   const int64_t P = (Sk + 15) / 16;  // compact bias cells per side
   if (pair) {
     // the projection inside the attention kernel: its fast path only
-    if (!fast || Dv != 128)
-      return fail(ABG_ERR_UNSUPPORTED,
-                  "the pair form is implemented for ABG_BF16 with softcap > 0 and Dv = 128 only");
+    if (!fast)
+      return fail(ABG_ERR_UNSUPPORTED, "the pair form is implemented for ABG_BF16 with softcap > 0 only");
     if (C != 128) return fail(ABG_ERR_UNSUPPORTED, "C = %lld: only 128 pair channels are supported", (long long)C);
   }
   // per-item block of the bias (elements) or of the pair representation

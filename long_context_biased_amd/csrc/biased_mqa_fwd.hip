@@ -987,10 +987,13 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUS
   // past the end the copies are clamped and land where nobody reads again
   issue_kv<HPW, DV, TAIL, FUSED, NN>(smem, c, min(t + 2, last));
   issue_cells<HPW, DV, TAIL, FUSED, C>(smem, c, min(t + 3, last));
+  // pair vectors of tile t+2: read during X (value width 128), or after it
+  // (192, whose stage leaves no registers for them)
   bf16x8 pv[2];
-  if constexpr (FUSED) pair_load<DV, NN>(smem, pv);  // pair vectors of tile t+2, read during X
+  if constexpr (FUSED && DV == 128) pair_load<DV, NN>(smem, pv);
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
   fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, P1, ring);
+  if constexpr (FUSED && DV != 128) pair_load<DV, NN>(smem, pv);
   // the exponent offsets of tile t+2, read by the next iteration
   if constexpr (FUSED) pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
   else expand_bias<HPW, DV, NN>(smem, c.wave, c.beta_mul);
@@ -1414,11 +1417,9 @@ template <int DV>
 hipError_t launch_fast(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
                        float den_a) {
   const bool tail = a.Sk % kTileKeys != 0 || a.Sq % kBlockPos != 0;
-  if constexpr (DV == 128) {
-    if (a.pair)  // bias projected in the kernel from the pair representation
-      return tail ? launch_fast_t<DV, true, true>(a, stream, alpha, beta_mul, den_a)
-                  : launch_fast_t<DV, false, true>(a, stream, alpha, beta_mul, den_a);
-  }
+  if (a.pair)  // bias projected in the kernel from the pair representation
+    return tail ? launch_fast_t<DV, true, true>(a, stream, alpha, beta_mul, den_a)
+                : launch_fast_t<DV, false, true>(a, stream, alpha, beta_mul, den_a);
   return tail ? launch_fast_t<DV, true, false>(a, stream, alpha, beta_mul, den_a)
               : launch_fast_t<DV, false, false>(a, stream, alpha, beta_mul, den_a);
 }

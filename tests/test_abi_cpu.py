@@ -138,7 +138,7 @@ def pattn(**kw):
 # stay invalid: the pointers are not device memory.
 PAIR_CASES = [
     (dict(pair=None), NULL), (dict(weight=None), NULL), (dict(q=None), NULL), (dict(out=None), NULL),
-    (dict(dtype=F32), UNSUP), (dict(softcap=0.0), UNSUP), (dict(Dv=192), UNSUP),
+    (dict(dtype=F32), UNSUP), (dict(softcap=0.0), UNSUP), (dict(Dv=256), UNSUP),
     (dict(C=64), UNSUP), (dict(C=256), UNSUP), (dict(dtype=5), VALUE),
     (dict(Sk=0), SHAPE), (dict(Sq=0), SHAPE), (dict(kv_splits=3), SHAPE),
     (dict(kv_splits=8, ws=None), NULL),

@@ -340,8 +340,10 @@ def test_attention_tails_full_sampled(S):
 # The projection inside the attention kernel (pair form): no bias tensor
 # ---------------------------------------------------------------------------
 PAIR = [
-    # B, S, q_rows (start, stop) or None, kv_splits, n_pairs
+    # B, S, q_rows (start, stop) or None, kv_splits, n_pairs[, Dv]
     (1, 2048, None, 1, None),
+    (1, 1000, None, 1, None, 192),   # the checkpoint's value width, a tail
+    (2, 768, (64, 500), 3, 1, 192),  # ... a query block, key ranges, a shared pair
     (2, 512, None, 1, 1),            # two items share one pair block
     (4, 256, None, 2, 2),            # pairs of items share a block (the variant's layout)
     (1, 1000, None, 1, None),        # lengths off the tile grid
@@ -367,11 +369,12 @@ def _run_pair(L, rows, z):
     return to_host(out), to_host(two)
 
 
-@pytest.mark.parametrize("case", PAIR, ids=lambda c: "B%d_S%d_q%s_z%s_pairs%s" % c)
+@pytest.mark.parametrize("case", PAIR, ids=lambda c: "B%d_S%d_q%s_z%s_pairs%s" % c[:5] + ("_dv%d" % c[5] if len(c) > 5 else ""))
 def test_pair_form(case):
-    B, S, qr, z, n_pairs = case
+    B, S, qr, z, n_pairs = case[:5]
+    Dv = case[5] if len(case) > 5 else 128
     L = workloads.make_custom(B=B, S=S, dtype="bf16", C=128, seed=700 + S + B, qkv_std=1.0,
-                              bias_std=2.0, n_pairs=n_pairs)
+                              bias_std=2.0, n_pairs=n_pairs, Dv=Dv)
     rows = range(0, S) if qr is None else range(*qr)
     out, two = _run_pair(L, rows, z)
     bias64 = _oracle_bias(L)

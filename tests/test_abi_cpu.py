@@ -228,3 +228,26 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+def test_plain_c_consumer(tmp_path):
+    """The boundary is usable from C alone: a C99 program built with
+    -pedantic -Werror against include/abg.h, linked to the library, gets the
+    same host-side validation results as the Python binding."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not on PATH")
+    abg.load()
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = str(tmp_path / "c_consumer")
+    subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_consumer.c"),
+                    "-L", libdir, "-labg", "-Wl,-rpath," + libdir, "-o", exe],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert "c consumer ok" in r.stdout

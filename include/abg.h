@@ -111,9 +111,8 @@ abg_status abg_pair_bias_project(const void* pair, const void* weight, float* bi
  *         REF/ALT pair).
  *   out   [B, S, Hq, Dv]  dtype, written fully; must not overlap any input.
  *
- * Non-causal, no masks.  Limits (v1): B >= 1; 1 <= S <= 262144, and
- * S % 64 == 0 unless dtype is ABG_BF16 with softcap > 0 (that path takes
- * any length); Hq == 8; Dk == 128; Dv == 128, or Dv == 192 (the released
+ * Non-causal, no masks.  Limits (v1): B >= 1; 1 <= S <= 262144 (any
+ * length: a sequence may end inside a 64-key tile); Hq == 8; Dk == 128; Dv == 128, or Dv == 192 (the released
  * checkpoint's value width, same page, section "Why stock FlashAttention
  * was not a drop-in replacement") for ABG_BF16 with softcap > 0;
  * bias_group >= 1 and bias_batch_stride == 0 or >= Hq*P^2 (a multiple of
@@ -156,8 +155,7 @@ int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, in
  *         scratch and are overwritten.  Calls that share a workspace must be
  *         ordered on one stream.
  *
- * Limits beyond abg_biased_mqa_fwd's: 1 <= Sq <= Sk, Sq a multiple of 32
- * unless dtype is ABG_BF16 with softcap > 0; q_offset a multiple of 16 with
+ * Limits beyond abg_biased_mqa_fwd's: 1 <= Sq <= Sk; q_offset a multiple of 16 with
  * q_offset + Sq <= Sk; 1 <= kv_splits <= 64 dividing ceil(Sk/64);
  * kv_splits > 1 for ABG_BF16 with softcap > 0 only.
  * abg_biased_mqa_fwd(...) equals abg_biased_mqa_fwd_ex(..., NULL, 0, B, S, S,

@@ -61,20 +61,13 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   if (B < 1 || B > 65535) return fail(ABG_ERR_SHAPE, "B = %lld must be in [1, 65535]", (long long)B);
   if (!std::isfinite(softcap) || softcap < 0.f)
     return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
-  // the bf16 path with the cap takes any length; the others whole tiles
+  // the bf16 path with the cap (the fast kernel) also takes value width 192
+  // and key ranges; every path takes any length
   const bool fast = dtype == ABG_BF16 && softcap > 0.f;
   if (Sk < 1 || Sk > 262144)
     return fail(ABG_ERR_SHAPE, "S = %lld must be in [1, 262144]", (long long)Sk);
-  if (!fast && Sk % 64 != 0)
-    return fail(ABG_ERR_UNSUPPORTED,
-                "S = %lld: lengths that are not a multiple of 64 are implemented for bf16 inputs with "
-                "softcap > 0 only", (long long)Sk);
   if (Sq < 1 || Sq > Sk)
     return fail(ABG_ERR_SHAPE, "Sq = %lld must be in [1, Sk = %lld]", (long long)Sq, (long long)Sk);
-  if (!fast && Sq % 32 != 0)
-    return fail(ABG_ERR_UNSUPPORTED,
-                "Sq = %lld: query counts that are not a multiple of 32 are implemented for bf16 inputs "
-                "with softcap > 0 only", (long long)Sq);
   if (q_offset < 0 || q_offset > Sk - Sq)
     return fail(ABG_ERR_SHAPE, "q_offset = %lld must be in [0, Sk - Sq = %lld]", (long long)q_offset,
                 (long long)(Sk - Sq));

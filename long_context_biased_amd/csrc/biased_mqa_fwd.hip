@@ -162,22 +162,50 @@ struct StageAddr {
   int v_glb;       // bytes from the V tile base to this thread's first V row
   int v_lds;       // LDS byte offset of the first V^T row of this thread's block
   int64_t b_glb;   // element offset of this thread's bias cell (tile 0)
+  // for sequences that end inside a tile: key rows are clamped to the last
+  // one, key cells to the last cell
+  int k_row;       // key row (within a tile) of this thread's first K chunk
+  int k_cb;        // byte offset of that chunk within its row
+  int v_row;       // first of the 4 key rows of this thread's V block
+  int v_cb;        // byte offset of its 4 value channels within a row
+  int64_t b_row;   // element offset of this thread's bias row (cell 0)
+  int b_cell;      // key cell of this thread within a tile
 };
 
-template <typename T>
+// TAIL: the sequence may end inside tile t (S keys, P cells); rows and cells
+// past the end read the last ones, so the stage holds finite data there.
+template <typename T, bool TAIL>
 __device__ __forceinline__ void load_tile(Staged<T>& st, const StageAddr& ad, const char* kb,
                                           const char* vb, const float* bias_b, int t, int tid,
-                                          float beta_mul) {
+                                          float beta_mul, int S, int P) {
   using L = Lay<T>;
-  const char* kt = kb + (int64_t)t * kTileKeys * L::K_ROW;
+  if constexpr (TAIL) {
+    const int key0 = t * kTileKeys;
 #pragma unroll
-  for (int i = 0; i < L::K_PT; ++i)
-    st.k[i] = *reinterpret_cast<const u32x4*>(kt + (tid + kThreads * i) * 16);
-  const char* vt = vb + (int64_t)t * kTileKeys * kD * L::E + ad.v_glb;
+    for (int i = 0; i < L::K_PT; ++i) {
+      const int key = min(key0 + ad.k_row + i * L::K_ROWS_PER_PASS, S - 1);
+      st.k[i] = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * L::K_ROW + ad.k_cb);
+    }
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    st.v[e] = *reinterpret_cast<const typename Traits<T>::VRow*>(vt + e * kD * L::E);
-  st.bias = bias_b[ad.b_glb + t * 4] * beta_mul;
+    for (int e = 0; e < 4; ++e) {
+      const int key = min(key0 + ad.v_row + e, S - 1);
+      st.v[e] = *reinterpret_cast<const typename Traits<T>::VRow*>(
+          vb + (int64_t)key * kD * L::E + ad.v_cb);
+    }
+    st.bias = bias_b[ad.b_row + min(t * 4 + ad.b_cell, P - 1)] * beta_mul;
+  } else {
+    (void)S;
+    (void)P;
+    const char* kt = kb + (int64_t)t * kTileKeys * L::K_ROW;
+#pragma unroll
+    for (int i = 0; i < L::K_PT; ++i)
+      st.k[i] = *reinterpret_cast<const u32x4*>(kt + (tid + kThreads * i) * 16);
+    const char* vt = vb + (int64_t)t * kTileKeys * kD * L::E + ad.v_glb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      st.v[e] = *reinterpret_cast<const typename Traits<T>::VRow*>(vt + e * kD * L::E);
+    st.bias = bias_b[ad.b_glb + t * 4] * beta_mul;
+  }
 }
 
 template <typename T>
@@ -258,10 +286,13 @@ __device__ __forceinline__ bf16x2 mask_pair(bf16x2 p, int k, int lim) {
 // Soft-capped weights exp(L - cap) of 16 scores (key cells beta.x for x < 8,
 // beta.y for x >= 8), packed as the PV operand; the row sum adds the packed
 // values.
-template <typename T>
+// Value x of a lane holds key 16 (x >> 3) + 8 g + (x & 7) of the half; with
+// MASK, keys at or past `lim` (counted from the half's first key, less 8 g)
+// get weight 0.
+template <typename T, bool MASK>
 __device__ __forceinline__ void softmax_capped(const f32x16& s, f32x2 beta, float alpha,
                                                float den_a, float& rowsum,
-                                               typename Traits<T>::F (&p)[2]) {
+                                               typename Traits<T>::F (&p)[2], int lim) {
   float w[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
@@ -269,6 +300,7 @@ __device__ __forceinline__ void softmax_capped(const f32x16& s, f32x2 beta, floa
     const float y = __builtin_amdgcn_exp2f(t2);
     const float d = __builtin_fmaf(y, den_a, den_a);
     w[x] = __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(d));
+    if constexpr (MASK) w[x] = 16 * (x >> 3) + (x & 7) < lim ? w[x] : 0.f;
   }
   if constexpr (sizeof(T) == 2) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -301,15 +333,19 @@ __device__ __forceinline__ void softmax_capped(const f32x16& s, f32x2 beta, floa
 
 // Uncapped online softmax of one 32-key half: returns the factor by which the
 // running numerator must be rescaled.
-template <typename T>
+// With MASK, keys past the end (as in softmax_capped) get exponent -inf:
+// weight 0, and no part in the maximum.  The row's first half always holds
+// key 0, so the running maximum is finite from the first half on.
+template <typename T, bool MASK>
 __device__ __forceinline__ float softmax_online(const f32x16& s, f32x2 beta, float alpha,
                                                 float& mrun, float& rowsum,
-                                                typename Traits<T>::F (&p)[2]) {
+                                                typename Traits<T>::F (&p)[2], int lim) {
   float u[16];
   float mt = -__builtin_inff();
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     u[x] = __builtin_fmaf(s[x], alpha, x < 8 ? beta.x : beta.y);
+    if constexpr (MASK) u[x] = 16 * (x >> 3) + (x & 7) < lim ? u[x] : -__builtin_inff();
     mt = __builtin_fmaxf(mt, u[x]);
   }
   mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
@@ -331,17 +367,17 @@ __device__ __forceinline__ float softmax_online(const f32x16& s, f32x2 beta, flo
   return sc;
 }
 
-template <typename T, bool CAPPED>
+template <typename T, bool CAPPED, bool MASK>
 __device__ __forceinline__ void softmax_half(const f32x16& s, f32x2 beta, float alpha, float den_a,
                                              float& mrun, float& rowsum, f32x16 (&O)[4],
-                                             typename Traits<T>::F (&p)[2]) {
+                                             typename Traits<T>::F (&p)[2], int lim) {
   if constexpr (CAPPED) {
     (void)mrun;
     (void)O;
-    softmax_capped<T>(s, beta, alpha, den_a, rowsum, p);
+    softmax_capped<T, MASK>(s, beta, alpha, den_a, rowsum, p, lim);
   } else {
     (void)den_a;
-    const float sc = softmax_online<T>(s, beta, alpha, mrun, rowsum, p);
+    const float sc = softmax_online<T, MASK>(s, beta, alpha, mrun, rowsum, p, lim);
 #pragma unroll
     for (int db = 0; db < 4; ++db) O[db] *= sc;
   }
@@ -456,7 +492,10 @@ __device__ __forceinline__ void copy_output(const char* smem, T* __restrict__ ou
   }
 }
 
-template <typename T, bool CAPPED>
+// TAIL: S need not be a multiple of the 64-key tile nor Sq of the 32-query
+// block.  Key rows and cells past the end are clamped when staged and their
+// weights masked to 0; query rows past Sq read row Sq - 1 and are not stored.
+template <typename T, bool CAPPED, bool TAIL>
 __global__ __launch_bounds__(kThreads, 1)
 void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
                            const T* __restrict__ v, const float* __restrict__ bias,
@@ -477,8 +516,11 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int b = blockIdx.y;
   const int qpos0 = blockIdx.x * kBlockPos;  // first row of this block in q / out
   const int pos0 = q_offset + qpos0;         // its position in the sequence
-  const int P = S >> 4;
-  const int n = S / kTileKeys;
+  const int P = (S + 15) >> 4;
+  const int n = (S + kTileKeys - 1) / kTileKeys;
+  // keys of the sequence from a half's first key on, less 8 g, is
+  // lim0 - (that key's index)
+  const int lim0 = S - 8 * g;
 
   const char* kb_ptr = reinterpret_cast<const char*>(k + (int64_t)b * S * kD);
   const char* vb_ptr = reinterpret_cast<const char*>(v + (int64_t)b * S * kD);
@@ -487,7 +529,8 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // ---- Q fragments (B operand), held for the whole kernel -----------------
   F qf[kD / 16];
   {
-    const char* qrow = reinterpret_cast<const char*>(q + (((int64_t)b * Sq + qpos0 + r) * kHeads + h) * kD);
+    const int qi = TAIL ? min(qpos0 + r, Sq - 1) : qpos0 + r;
+    const char* qrow = reinterpret_cast<const char*>(q + (((int64_t)b * Sq + qi) * kHeads + h) * kD);
 #pragma unroll
     for (int kc = 0; kc < kD / 16; ++kc) {
       const char* p = qrow + (kc * 16 + 8 * g) * E;
@@ -511,6 +554,8 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const int key = tid / L::K_CHUNKS;
     const int row = (key & ~31) | key_perm(key & 31);
     ad.k_lds = row * L::K_STRIDE + (tid % L::K_CHUNKS) * 16;
+    ad.k_row = key;
+    ad.k_cb = (tid % L::K_CHUNKS) * 16;
   }
   {
     // 4x4 block: keys 4kg.., channels 4dvg..; lanes run over kg first so the
@@ -520,9 +565,13 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const int dvg = ((lane6 >> 3) & 7) | ((w >> 1) << 3);
     ad.v_glb = (kg * 4) * kD * E + dvg * 4 * E;
     ad.v_lds = L::K_BYTES + (dvg * 4) * L::VT_STRIDE + kg * 4 * E;
+    ad.v_row = kg * 4;
+    ad.v_cb = dvg * 4 * E;
     const int bt = tid & 63;
     const int bh = bt >> 3, pb = (bt >> 2) & 1, cell = bt & 3;
     ad.b_glb = ((int64_t)bh * P + (pos0 >> 4) + pb) * P + cell;
+    ad.b_row = ((int64_t)bh * P + min((pos0 >> 4) + pb, P - 1)) * P;
+    ad.b_cell = cell;
   }
   // per-lane A fragment bases inside a stage (lane r reads LDS row r, which
   // holds key key_perm(r) of the 32-key half)
@@ -544,11 +593,11 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // block for the instruction scheduler.
   Staged<T> st;
   const int last = n - 1;
-  load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, 0, tid, beta_mul);
+  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, 0, tid, beta_mul, S, P);
   store_tile<T>(st, ad, smem, tid);
-  load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(1, last), tid, beta_mul);
+  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(1, last), tid, beta_mul, S, P);
   store_tile<T>(st, ad, smem + L::STAGE, tid);
-  load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(2, last), tid, beta_mul);
+  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(2, last), tid, beta_mul, S, P);
   __syncthreads();
 
   f32x16 S0 = qk_half<T>(smem, kbase, qf, 0);
@@ -556,7 +605,7 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   F P0[2], P1[2];
   {
     const f32x2 beta = *reinterpret_cast<const f32x2*>(smem + bias_lds);
-    softmax_half<T, CAPPED>(S0, beta, alpha, den_a, mrun, rowsum, O, P0);
+    softmax_half<T, CAPPED, TAIL>(S0, beta, alpha, den_a, mrun, rowsum, O, P0, lim0);
   }
 
   int cur = 0;  // buffer of tile t
@@ -568,26 +617,28 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
       if constexpr (NBUF == 3) {
         const int nn = (nxt + 1 == NBUF) ? 0 : nxt + 1;
         store_tile<T>(st, ad, smem + nn * L::STAGE, tid);
-        load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(t + 3, last), tid, beta_mul);
+        load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(t + 3, last), tid, beta_mul, S, P);
       }
       // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1)
       pv_half<T>(bcur, vbase, P0, O, 0);
       S0 = qk_half<T>(bnxt, kbase, qf, 0);
       {
         const f32x2 beta = *reinterpret_cast<const f32x2*>(bcur + bias_lds + 8);
-        softmax_half<T, CAPPED>(S1, beta, alpha, den_a, mrun, rowsum, O, P1);
+        softmax_half<T, CAPPED, TAIL>(S1, beta, alpha, den_a, mrun, rowsum, O, P1,
+                                      lim0 - t * kTileKeys - 32);
       }
       // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0)
       pv_half<T>(bcur, vbase, P1, O, 1);
       S1 = qk_half<T>(bnxt, kbase, qf, 1);
       {
         const f32x2 beta = *reinterpret_cast<const f32x2*>(bnxt + bias_lds);
-        softmax_half<T, CAPPED>(S0, beta, alpha, den_a, mrun, rowsum, O, P0);
+        softmax_half<T, CAPPED, TAIL>(S0, beta, alpha, den_a, mrun, rowsum, O, P0,
+                                      lim0 - (t + 1) * kTileKeys);
       }
       if constexpr (NBUF == 2) {
         __syncthreads();  // every wave is done with tile t: its buffer is free
         store_tile<T>(st, ad, smem + cur * L::STAGE, tid);
-        load_tile<T>(st, ad, kb_ptr, vb_ptr, bias_b, min(t + 3, last), tid, beta_mul);
+        load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(t + 3, last), tid, beta_mul, S, P);
       }
       __syncthreads();
       cur = nxt;
@@ -598,14 +649,16 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const char* bcur = smem + cur * L::STAGE;
     pv_half<T>(bcur, vbase, P0, O, 0);
     const f32x2 beta = *reinterpret_cast<const f32x2*>(bcur + bias_lds + 8);
-    softmax_half<T, CAPPED>(S1, beta, alpha, den_a, mrun, rowsum, O, P1);
+    softmax_half<T, CAPPED, TAIL>(S1, beta, alpha, den_a, mrun, rowsum, O, P1,
+                                  lim0 - last * kTileKeys - 32);
     pv_half<T>(bcur, vbase, P1, O, 1);
   }
   __syncthreads();  // the output staging below reuses the tile buffers
 
   stage_output<T>(smem, O, rowsum, r, g, h);
   __syncthreads();
-  copy_output<T, kThreads>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * kD, tid);
+  copy_output<T, kThreads>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * kD, tid,
+                           TAIL ? min(kBlockPos, Sq - qpos0) : kBlockPos);
 }
 
 // ===========================================================================
@@ -1441,12 +1494,13 @@ hipError_t launch_typed(const AttnLaunch& a, hipStream_t stream) {
     return a.Dv == 192 ? launch_fast<192>(a, stream, alpha, beta_mul, den_a)
                        : launch_fast<128>(a, stream, alpha, beta_mul, den_a);
   } else {
-    dim3 grid((unsigned)(a.Sq / kBlockPos), (unsigned)a.B);
-    hipLaunchKernelGGL((biased_mqa_fwd_kernel<T, CAPPED>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.bias, static_cast<T*>(a.out), (int)a.Sq,
-                       (int)a.Sk, (int)a.q_offset, a.bias_batch_stride, (int)a.bias_group, alpha,
-                       beta_mul, den_a);
+    const bool tail = a.Sk % kTileKeys != 0 || a.Sq % kBlockPos != 0;
+    dim3 grid((unsigned)((a.Sq + kBlockPos - 1) / kBlockPos), (unsigned)a.B);
+    auto kern = tail ? biased_mqa_fwd_kernel<T, CAPPED, true> : biased_mqa_fwd_kernel<T, CAPPED, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.bias,
+                       static_cast<T*>(a.out), (int)a.Sq, (int)a.Sk, (int)a.q_offset,
+                       a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
     return hipGetLastError();
   }
 }

@@ -59,9 +59,9 @@ ATTN_CASES = [
     (dict(bias=None), NULL), (dict(out=None), NULL),
     (dict(B=0), SHAPE), (dict(B=70000), SHAPE),
     (dict(S=0), SHAPE), (dict(S=-64), SHAPE), (dict(S=262144 + 64), SHAPE),
-    # lengths off the 64-key tile: only the bf16 path with the cap takes them
-    (dict(S=8192 + 16, dtype=F32), UNSUP), (dict(S=100, softcap=0.0), UNSUP),
-    (dict(S=32, dtype=F32), UNSUP),
+    # the generic kernel takes any length, but not value width 192
+    (dict(S=8192 + 16, dtype=F32, Dv=192), UNSUP), (dict(S=100, softcap=0.0, Dv=192), UNSUP),
+    (dict(S=32, dtype=F32, bias_batch_stride=4), SHAPE),
     (dict(Hq=4), UNSUP), (dict(Hq=16), UNSUP),
     # (every case here must stay invalid: the pointers are not device memory)
     (dict(Dk=64), UNSUP), (dict(Dv=64), UNSUP), (dict(Dv=256), UNSUP),
@@ -102,13 +102,13 @@ def attn_ex(**kw):
 
 # Every case must stay invalid: the pointers are not device memory.
 ATTN_EX_CASES = [
-    (dict(Sq=1000, dtype=F32, kv_splits=1), UNSUP), (dict(Sq=0), SHAPE), (dict(Sq=8192 + 32), SHAPE),
+    (dict(Sq=1000, dtype=F32, kv_splits=2), UNSUP), (dict(Sq=0), SHAPE), (dict(Sq=8192 + 32), SHAPE),
     (dict(q_offset=8), UNSUP), (dict(q_offset=-16), SHAPE), (dict(q_offset=8192 - 1024 + 16), SHAPE),
     (dict(kv_splits=0), SHAPE), (dict(kv_splits=65), SHAPE), (dict(kv_splits=3), SHAPE),
     (dict(dtype=F32), UNSUP), (dict(softcap=0.0), UNSUP),
     (dict(ws=None), NULL), (dict(ws_bytes=1024), SHAPE), (dict(ws=WS + 8), ALIGN),
     (dict(ws=Q), ALIAS), (dict(ws=OUT - 1024), ALIAS),
-    (dict(Sk=8192 + 16, dtype=F32, kv_splits=1), UNSUP), (dict(Dv=192, dtype=F32, kv_splits=1), UNSUP),
+    (dict(Sk=8192 + 64, dtype=F32, kv_splits=3), UNSUP), (dict(Dv=192, dtype=F32, kv_splits=1), UNSUP),
     # 8192 + 16 keys make 129 tiles, which 8 ranges do not divide
     (dict(Sk=8192 + 16), SHAPE), (dict(Sk=100, Sq=64, q_offset=0, kv_splits=4), SHAPE),
     (dict(q=None), NULL), (dict(out=Q), ALIAS),

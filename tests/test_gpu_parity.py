@@ -300,6 +300,58 @@ def test_attention_tails(case):
     print(f"  tails {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
 
 
+# The generic kernel (float32 inputs, or no cap) off the tile grid: the same
+# clamped staging and masking, with the online recurrence when uncapped (a
+# masked key must take no part in the running maximum either).
+GENERIC_TAILS = [
+    # dtype, cap, B, S, q_rows (start, stop) or None
+    ("f32", 5.0, 1, 1, None),           # one key, one query
+    ("f32", 0.0, 1, 17, None),          # one tile, its last key in the first half
+    ("bf16", 0.0, 2, 48, None),         # ... in the second half
+    ("f32", 5.0, 1, 100, None),         # the partial tile in LDS stage 1 (of 2)
+    ("f32", 0.0, 1, 150, None),         # ... stage 0
+    ("bf16", 0.0, 1, 200, None),        # bf16 uncapped: 3 stages, the partial in stage 0
+    ("bf16", 0.0, 1, 260, None),        # ... stage 1, 4 keys in it
+    ("f32", 0.0, 2, 777, None),         # two items with their own bias blocks
+    ("f32", 5.0, 1, 1000, (16, 61)),    # 45 queries at an offset
+    ("bf16", 0.0, 1, 1000, (960, 1000)),
+    ("f32", 5.0, 1, 64, (32, 45)),      # whole tiles, 13 queries
+    ("f32", 0.0, 1, 1023, None),
+]
+
+
+@pytest.mark.parametrize("case", GENERIC_TAILS, ids=lambda c: "%s_cap%g_B%d_S%d_q%s" % c)
+def test_generic_kernel_tails(case):
+    dt, cap, B, S, qr = case
+    L = workloads.make_custom(B=B, S=S, dtype=dt, C=16, seed=1300 + S + B, qkv_std=1.0,
+                              bias_std=2.0)
+    L.cap = cap
+    rows = range(0, S) if qr is None else range(*qr)
+    Sq = rows.stop - rows.start
+    t = upload(L)
+    bias = pair_bias_project(t["pair"], t["weight"])
+    q = t["q"][:, rows.start:rows.stop].contiguous()
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    pad = 5
+    buf = torch.full((B, Sq + pad, 8, 128), float("nan"), dtype=tdt, device="cuda")
+    out_t = buf[:, :Sq] if B == 1 else torch.empty((B, Sq, 8, 128), dtype=tdt, device="cuda")
+    biased_mqa_fwd(q, t["k"], t["v"], bias, out_t, scale=L.scale, softcap=cap,
+                   q_offset=rows.start)
+    torch.cuda.synchronize()
+    if B == 1:
+        assert torch.isnan(buf[:, Sq:].float()).all(), "rows past Sq were written"
+    out = to_host(out_t)
+    bias64 = _oracle_bias(L)
+    worst = (0.0, 0.0)
+    for b in range(B):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, np.arange(rows.start, rows.stop),
+                                    scale=L.scale, cap=cap, batch=b)
+        ok, ma, rel = attention_ok(out[b], ref, dt)
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+        worst = (max(worst[0], ma), max(worst[1], rel))
+    print(f"  generic tails {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
+
+
 def test_attention_long_sampled():
     """S = 65536 (4096 compact cells per side, 1024 key tiles, a 512 MiB
     bias), far past the workloads' lengths: sampled rows, through the

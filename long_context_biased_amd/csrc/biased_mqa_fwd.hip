@@ -81,7 +81,10 @@ constexpr int kTileKeys = 64;  // keys per LDS tile
 constexpr int kBlockPos = 32;  // query positions per workgroup
 constexpr int kThreads = 64 * kHeads;
 constexpr float kLog2e = 1.4426950408889634f;
-// Heads per wave of the bf16 soft-capped kernel (2: four waves, one per SIMD).
+// Heads per wave of the bf16 soft-capped kernel.  1 (built): eight waves, two
+// per SIMD.  2: four waves, one per SIMD, each LDS fragment feeding two
+// MFMAs; it compiles, spills a few registers and runs about a third slower
+// (one wave per SIMD cannot hide the softmax's latencies).
 #ifndef ABG_FAST_HPW
 #define ABG_FAST_HPW 1
 #endif

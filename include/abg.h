@@ -115,8 +115,8 @@ abg_status abg_pair_bias_project(const void* pair, const void* weight, float* bi
  * length: a sequence may end inside a 64-key tile); Hq == 8; Dk == 128; Dv == 128, or Dv == 192 (the released
  * checkpoint's value width, same page, section "Why stock FlashAttention
  * was not a drop-in replacement") for ABG_BF16 with softcap > 0;
- * bias_group >= 1 and bias_batch_stride == 0 or >= Hq*P^2 (a multiple of
- * 4); scale finite; softcap finite and >= 0.  Any other request returns
+ * bias_group >= 1 and bias_batch_stride == 0 or in [Hq*P^2, 2^40] (a
+ * multiple of 4); scale finite; softcap finite and >= 0.  Any other request returns
  * ABG_ERR_UNSUPPORTED, ABG_ERR_SHAPE or ABG_ERR_VALUE before anything is
  * enqueued.
  */
@@ -157,7 +157,8 @@ int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, in
  *
  * Limits beyond abg_biased_mqa_fwd's: 1 <= Sq <= Sk; q_offset a multiple of 16 with
  * q_offset + Sq <= Sk; 1 <= kv_splits <= 64 dividing ceil(Sk/64);
- * kv_splits > 1 for ABG_BF16 with softcap > 0 only.
+ * kv_splits > 1 for ABG_BF16 with softcap > 0 only, and with
+ * B * Sq * Hq * Dv / 4 < 2^39.
  * abg_biased_mqa_fwd(...) equals abg_biased_mqa_fwd_ex(..., NULL, 0, B, S, S,
  * 0, ..., 1, ...). */
 abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
@@ -184,7 +185,8 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
  *   weight  [C, Hq]       bf16
  *
  * Limits beyond abg_biased_mqa_fwd_ex's: dtype ABG_BF16 with softcap > 0;
- * Dv == 128 or 192; C == 128; pair_batch_stride 0 or >= P*P*C and a multiple of 8;
+ * Dv == 128 or 192; C == 128; pair_batch_stride 0 or in [P*P*C, 2^40] and a
+ * multiple of 8;
  * 1 <= pair_group <= B; pair and weight 16-byte aligned and not overlapping
  * out or the workspace.  kv_splits, q_offset and the workspace work as for
  * abg_biased_mqa_fwd_ex. */

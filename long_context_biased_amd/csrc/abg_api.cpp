@@ -93,6 +93,11 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   if (kv_splits > 1 && workspace_bytes < ws_need)
     return fail(ABG_ERR_SHAPE, "workspace_bytes = %lld, need %lld", (long long)workspace_bytes,
                 (long long)ws_need);
+  // the merge of the partials runs one thread per 4 output values in a
+  // one-dimensional grid of 256-thread workgroups
+  if (kv_splits > 1 && B * Sq * Hq * (Dv / 4) > (int64_t)INT32_MAX * 256)
+    return fail(ABG_ERR_SHAPE, "B * Sq = %lld query positions are too many for kv_splits > 1",
+                (long long)(B * Sq));
   if (bias_group < 1 || bias_group > B)
     return fail(ABG_ERR_SHAPE, "%s_group = %lld must be in [1, B]", pair ? "pair" : "bias",
                 (long long)bias_group);
@@ -105,6 +110,9 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   }
   // per-item block of the bias (elements) or of the pair representation
   const int64_t bias_elems = pair ? P * P * C : Hq * P * P;
+  if (bias_batch_stride < 0 || bias_batch_stride > (int64_t(1) << 40))
+    return fail(ABG_ERR_SHAPE, "%s_batch_stride = %lld must be in [0, 2^40]", pair ? "pair" : "bias",
+                (long long)bias_batch_stride);
   if (bias_batch_stride != 0 && bias_batch_stride < bias_elems)
     return fail(ABG_ERR_SHAPE, "%s_batch_stride = %lld must be 0 or >= %lld", pair ? "pair" : "bias",
                 (long long)bias_batch_stride, (long long)bias_elems);

@@ -71,7 +71,8 @@ ATTN_CASES = [
     (dict(softcap=float("nan")), VALUE),
     (dict(dtype=7), VALUE),
     (dict(bias_group=0), SHAPE), (dict(B=2, bias_group=3), SHAPE),
-    (dict(B=2, bias_batch_stride=100), SHAPE),
+    (dict(B=2, bias_batch_stride=100), SHAPE), (dict(B=2, bias_batch_stride=(1 << 40) + 4), SHAPE),
+    (dict(bias_batch_stride=-4), SHAPE),
     (dict(B=2, bias_batch_stride=8 * 512 * 512 + 2), ALIGN),
     (dict(q=Q + 8), ALIGN), (dict(k=K + 4), ALIGN), (dict(v=V + 2), ALIGN),
     (dict(bias=BIAS + 12), ALIGN), (dict(out=OUT + 8), ALIGN),
@@ -112,6 +113,8 @@ ATTN_EX_CASES = [
     # 8192 + 16 keys make 129 tiles, which 8 ranges do not divide
     (dict(Sk=8192 + 16), SHAPE), (dict(Sk=100, Sq=64, q_offset=0, kv_splits=4), SHAPE),
     (dict(q=None), NULL), (dict(out=Q), ALIAS),
+    # more partial rows than the merge grid takes (checked before the overlaps)
+    (dict(B=65535, Sq=262144, Sk=262144, q_offset=0, kv_splits=2, ws_bytes=1 << 62), SHAPE),
 ]
 
 
@@ -143,6 +146,7 @@ PAIR_CASES = [
     (dict(Sk=0), SHAPE), (dict(Sq=0), SHAPE), (dict(kv_splits=3), SHAPE),
     (dict(kv_splits=8, ws=None), NULL),
     (dict(B=2, pair_batch_stride=100), SHAPE), (dict(B=2, pair_batch_stride=512 * 512 * 128 + 4), ALIGN),
+    (dict(B=2, pair_batch_stride=1 << 41), SHAPE),
     (dict(pair_group=0), SHAPE), (dict(B=2, pair_group=3), SHAPE),
     (dict(pair=BIAS + 8), ALIGN), (dict(weight=WS + 2), ALIGN), (dict(out=OUT + 8), ALIGN),
     (dict(out=BIAS), ALIAS), (dict(out=WS - 1024), ALIAS), (dict(out=Q), ALIAS),

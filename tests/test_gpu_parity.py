@@ -529,6 +529,35 @@ def test_equal_values_and_zero_logits(dt):
     assert np.all(np.abs(out - mean) <= rtol * np.abs(mean) + atol)
 
 
+@pytest.mark.parametrize("route,dt,cap", [("bias", "bf16", 5.0), ("bias", "f32", 5.0),
+                                          ("bias", "bf16", 0.0), ("bias", "f32", 0.0),
+                                          ("pair", "bf16", 5.0)])
+def test_saturated_logits(route, dt, cap):
+    """Bias cells far beyond the cap (std 60 against cap 5): the capped
+    logits sit at +-cap to within rounding, so exp2 of the tanh argument
+    overflows to inf or underflows to 0 in float32, and the weights must
+    still come out as exp(0) = 1 and exp(-2 cap); without the cap the
+    running maximum jumps by tens at a time.  300 positions: a partial last
+    tile and query block."""
+    L = workloads.make_custom(B=1, S=300, dtype=dt, C=128 if route == "pair" else 16,
+                              seed=4242, qkv_std=1.0, bias_std=60.0)
+    L.cap = cap
+    t = upload(L)
+    if route == "pair":
+        out = pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], scale=L.scale,
+                                  softcap=cap)
+    else:
+        bias = pair_bias_project(t["pair"], t["weight"])
+        out = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, scale=L.scale, softcap=cap)
+    torch.cuda.synchronize()
+    got = to_host(out)
+    bias64 = _oracle_bias(L)
+    assert float(np.abs(bias64).max()) > 20 * max(cap, 1.0)
+    ref = oracle.attention(L.q, L.k, L.v, bias64, scale=L.scale, cap=cap)
+    ok, ma, rel = attention_ok(got, ref, dt)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_deterministic_and_stream_ordered():
     """Bitwise-identical results across launches and on a side stream."""
     L = workloads.make_layer("full", layer=1)

@@ -144,10 +144,11 @@ int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, in
  *         equation (page "Making Full-Context AlphaGenome Fit on an RTX 3090",
  *         section "Why stock FlashAttention was not a drop-in replacement").
  *   kv_splits  the ceil(Sk/64) key tiles are divided into kv_splits equal ranges,
- *         each computed by its own workgroups; their partial softmax sums
- *         are merged afterwards (section "Online softmax, one block at a
- *         time": with the cap the maximum is fixed, so the partial
- *         numerators and denominators simply add).  This keeps the GPU full
+ *         each computed by its own workgroups; their partial softmax states
+ *         are merged afterwards by the update equations of section "Online
+ *         softmax, one block at a time" (with the cap the maximum is fixed,
+ *         so the partial numerators and denominators simply add; without it
+ *         each range's maximum is carried).  This keeps the GPU full
  *         when B * Sq / 32 is small (short sequences, one GPU's share of the
  *         queries).  kv_splits > 1 needs a device workspace of
  *         abg_biased_mqa_fwd_workspace_bytes(...) bytes, owned by the caller,
@@ -157,8 +158,7 @@ int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, in
  *
  * Limits beyond abg_biased_mqa_fwd's: 1 <= Sq <= Sk; q_offset a multiple of 16 with
  * q_offset + Sq <= Sk; 1 <= kv_splits <= 64 dividing ceil(Sk/64);
- * kv_splits > 1 for ABG_BF16 with softcap > 0 only, and with
- * B * Sq * Hq * Dv / 4 < 2^39.
+ * kv_splits > 1 needs B * Sq * Hq * Dv / 4 < 2^39.
  * abg_biased_mqa_fwd(...) equals abg_biased_mqa_fwd_ex(..., NULL, 0, B, S, S,
  * 0, ..., 1, ...). */
 abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,

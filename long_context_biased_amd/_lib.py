@@ -188,12 +188,12 @@ def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
     sequence whose ``k`` [B, Sk, 1, 128] and ``v`` [B, Sk, 1, Dv] (bfloat16 or
     float32; Dv 128, or 192 for bf16 with the cap) cover all Sk positions;
     Sq == Sk and q_offset == 0 is the plain call.  ``bias`` float32 compact
-    bias [8, Sk/16, Sk/16] shared by all items, or [Bb, 8, Sk/16, Sk/16] with
-    item b reading block b // bias_group.  ``scale`` defaults to
+    bias [8, P, P] (P = ceil(Sk/16)) shared by all items, or [Bb, 8, P, P]
+    with item b reading block b // bias_group.  ``scale`` defaults to
     1/sqrt(128); ``softcap`` 0 disables the cap.  ``kv_splits`` > 1 (or
-    "auto") computes key ranges in separate workgroups and merges them
-    (bf16 with the cap); the float32 workspace is ``workspace`` or a new
-    device tensor.  Returns ``out`` [B, Sq, 8, Dv] in the input dtype.
+    "auto") computes key ranges in separate workgroups and merges them; the
+    float32 workspace is ``workspace`` or a new device tensor.  Returns
+    ``out`` [B, Sq, 8, Dv] in the input dtype.
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (bias, "bias")):
@@ -230,7 +230,7 @@ def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
     if out.dtype != q.dtype or tuple(out.shape) != (B, Sq, Hq, Dv):
         raise ValueError("out must match q's dtype and be [B, Sq, Hq, Dv]")
     if kv_splits == "auto":
-        kv_splits = auto_kv_splits(B, Sq, Sk) if (q.dtype == torch.bfloat16 and softcap > 0) else 1
+        kv_splits = auto_kv_splits(B, Sq, Sk)
     kv_splits = int(kv_splits)
     if kv_splits == 1 and Sq == Sk and q_offset == 0 and workspace is None:
         _check(raw_biased_mqa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(),

@@ -62,7 +62,7 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   if (!std::isfinite(softcap) || softcap < 0.f)
     return fail(ABG_ERR_VALUE, "softcap must be finite and >= 0");
   // the bf16 path with the cap (the fast kernel) also takes value width 192
-  // and key ranges; every path takes any length
+  // and the pair form; every path takes any length and key ranges
   const bool fast = dtype == ABG_BF16 && softcap > 0.f;
   if (Sk < 1 || Sk > 262144)
     return fail(ABG_ERR_SHAPE, "S = %lld must be in [1, 262144]", (long long)Sk);
@@ -86,8 +86,6 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   if (tiles % kv_splits != 0)
     return fail(ABG_ERR_SHAPE, "kv_splits = %lld must divide the %lld key tiles", (long long)kv_splits,
                 (long long)tiles);
-  if (kv_splits > 1 && !fast)
-    return fail(ABG_ERR_UNSUPPORTED, "kv_splits > 1 is implemented for bf16 inputs with softcap > 0 only");
   const int64_t ws_need = abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits);
   if (kv_splits > 1 && !workspace) return fail(ABG_ERR_NULL, "workspace is NULL (kv_splits > 1)");
   if (kv_splits > 1 && workspace_bytes < ws_need)

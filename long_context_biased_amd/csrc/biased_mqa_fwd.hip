@@ -183,17 +183,19 @@ __device__ __forceinline__ void load_tile(Staged<T>& st, const StageAddr& ad, co
                                           float beta_mul, int S, int P) {
   using L = Lay<T>;
   if constexpr (TAIL) {
+    // 32-bit byte offsets from the item's base: S <= 2^18 rows of at most
+    // 512 bytes
     const int key0 = t * kTileKeys;
 #pragma unroll
     for (int i = 0; i < L::K_PT; ++i) {
       const int key = min(key0 + ad.k_row + i * L::K_ROWS_PER_PASS, S - 1);
-      st.k[i] = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * L::K_ROW + ad.k_cb);
+      st.k[i] = *reinterpret_cast<const u32x4*>(kb + (uint32_t)(key * L::K_ROW + ad.k_cb));
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int key = min(key0 + ad.v_row + e, S - 1);
       st.v[e] = *reinterpret_cast<const typename Traits<T>::VRow*>(
-          vb + (int64_t)key * kD * L::E + ad.v_cb);
+          vb + (uint32_t)(key * kD * L::E + ad.v_cb));
     }
     st.bias = bias_b[ad.b_row + min(t * 4 + ad.b_cell, P - 1)] * beta_mul;
   } else {
@@ -498,13 +500,18 @@ __device__ __forceinline__ void copy_output(const char* smem, T* __restrict__ ou
 // TAIL: S need not be a multiple of the 64-key tile nor Sq of the 32-query
 // block.  Key rows and cells past the end are clamped when staged and their
 // weights masked to 0; query rows past Sq read row Sq - 1 and are not stored.
-template <typename T, bool CAPPED, bool TAIL>
+// SPLIT: workgroup z of the grid takes key tiles [z n, z n + n) (n =
+// tiles_per_split) and writes its partial state to the workspace instead of
+// the output, for merge_partials_kernel: with the cap the numerator rows and
+// the denominators (the maximum is the fixed cap); without it the normalised
+// rows n / d and log2 d + m (m the running maximum, base 2).
+template <typename T, bool CAPPED, bool TAIL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1)
 void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
                            const T* __restrict__ v, const float* __restrict__ bias,
-                           T* __restrict__ out, int Sq, int S, int q_offset,
-                           int64_t bias_batch_stride, int bias_group, float alpha,
-                           float beta_mul, float den_a) {
+                           T* __restrict__ out, float* __restrict__ ws, int Sq, int S,
+                           int q_offset, int tiles_per_split, int64_t bias_batch_stride,
+                           int bias_group, float alpha, float beta_mul, float den_a) {
   using L = Lay<T>;
   using F = typename Traits<T>::F;
   constexpr int E = L::E;
@@ -520,7 +527,9 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int qpos0 = blockIdx.x * kBlockPos;  // first row of this block in q / out
   const int pos0 = q_offset + qpos0;         // its position in the sequence
   const int P = (S + 15) >> 4;
-  const int n = (S + kTileKeys - 1) / kTileKeys;
+  // this workgroup's key tiles: t0 .. last (tile indices in the sequence)
+  const int t0 = SPLIT ? (int)blockIdx.z * tiles_per_split : 0;
+  const int last = SPLIT ? t0 + tiles_per_split - 1 : (S + kTileKeys - 1) / kTileKeys - 1;
   // keys of the sequence from a half's first key on, less 8 g, is
   // lim0 - (that key's index)
   const int lim0 = S - 8 * g;
@@ -591,16 +600,15 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   float mrun = -__builtin_inff();
 
   // ---- prologue -----------------------------------------------------------------
-  // Tile indices past the end are clamped to the last tile: the extra loads
-  // and stores go to a buffer nobody reads, and the loop body stays one basic
-  // block for the instruction scheduler.
+  // Tile indices past the range are clamped to its last tile: the extra
+  // loads and stores go to a buffer nobody reads, and the loop body stays one
+  // basic block for the instruction scheduler.
   Staged<T> st;
-  const int last = n - 1;
-  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, 0, tid, beta_mul, S, P);
+  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, t0, tid, beta_mul, S, P);
   store_tile<T>(st, ad, smem, tid);
-  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(1, last), tid, beta_mul, S, P);
+  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(t0 + 1, last), tid, beta_mul, S, P);
   store_tile<T>(st, ad, smem + L::STAGE, tid);
-  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(2, last), tid, beta_mul, S, P);
+  load_tile<T, TAIL>(st, ad, kb_ptr, vb_ptr, bias_b, min(t0 + 2, last), tid, beta_mul, S, P);
   __syncthreads();
 
   f32x16 S0 = qk_half<T>(smem, kbase, qf, 0);
@@ -608,12 +616,13 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
   F P0[2], P1[2];
   {
     const f32x2 beta = *reinterpret_cast<const f32x2*>(smem + bias_lds);
-    softmax_half<T, CAPPED, TAIL>(S0, beta, alpha, den_a, mrun, rowsum, O, P0, lim0);
+    softmax_half<T, CAPPED, TAIL>(S0, beta, alpha, den_a, mrun, rowsum, O, P0,
+                                  lim0 - t0 * kTileKeys);
   }
 
   int cur = 0;  // buffer of tile t
   {
-    for (int t = 0; t < last; ++t) {
+    for (int t = t0; t < last; ++t) {
       const int nxt = (cur + 1 == NBUF) ? 0 : cur + 1;
       const char* bcur = smem + cur * L::STAGE;
       const char* bnxt = smem + nxt * L::STAGE;
@@ -656,12 +665,36 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                   lim0 - last * kTileKeys - 32);
     pv_half<T>(bcur, vbase, P1, O, 1);
   }
-  __syncthreads();  // the output staging below reuses the tile buffers
-
-  stage_output<T>(smem, O, rowsum, r, g, h);
-  __syncthreads();
-  copy_output<T, kThreads>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * kD, tid,
-                           TAIL ? min(kBlockPos, Sq - qpos0) : kBlockPos);
+  if constexpr (SPLIT) {
+    // partial rows [split][b][pos][h][128] and per-row values [split][b][pos][h],
+    // float32; lane (r, g) holds channels 32 db + 8 j + 4 g .. + 3 of its row
+    const int64_t rows = (int64_t)gridDim.y * Sq * kHeads;
+    const int64_t row = ((int64_t)blockIdx.z * gridDim.y + b) * Sq * kHeads +
+                        (int64_t)(qpos0 + r) * kHeads + h;
+    const float tot = rowsum + __shfl_xor(rowsum, 32);
+    if (!TAIL || qpos0 + r < Sq) {
+      // uncapped: store n / d and the row's log2-sum-exp, so that the merge
+      // needs no numerator scaling per range
+      const float inv = CAPPED ? 1.0f : 1.0f / tot;
+      float* nrow = ws + row * kD + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 x = {O[db][4 * j] * inv, O[db][4 * j + 1] * inv, O[db][4 * j + 2] * inv,
+                           O[db][4 * j + 3] * inv};
+          *reinterpret_cast<f32x4*>(nrow + 32 * db + 8 * j) = x;
+        }
+      if (g == 0) ws[(int64_t)gridDim.z * rows * kD + row] = CAPPED ? tot : mrun + __builtin_amdgcn_logf(tot);
+    }
+  } else {
+    (void)ws;
+    __syncthreads();  // the output staging below reuses the tile buffers
+    stage_output<T>(smem, O, rowsum, r, g, h);
+    __syncthreads();
+    copy_output<T, kThreads>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * kD, tid,
+                             TAIL ? min(kBlockPos, Sq - qpos0) : kBlockPos);
+  }
 }
 
 // ===========================================================================
@@ -1408,12 +1441,17 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   }
 }
 
-// out[b, i, h, :] = sum_z n[z, b, i, h, :] / sum_z d[z, b, i, h] (bf16): the
-// merge of key ranges computed with the same fixed maximum, which adds.  One
-// thread per 4 channels; HBM-bound.
-template <int DV>
+// Merge of the key ranges' partial states into the output (one thread per 4
+// channels of a row; HBM-bound), per the page's update equations for two
+// states (m, d, n) -> (max m, sum d e^(m - max m), sum n e^(m - max m)):
+//   * ranges computed with the same fixed maximum (the cap): numerators n_z
+//     and denominators d_z, which add: out = sum_z n_z / sum_z d_z;
+//   * LSE, ranges with their own running maxima m_z: normalised rows
+//     o_z = n_z / d_z and l_z = m_z + log2 d_z (base 2); with M = max_z l_z,
+//     out = sum_z 2^(l_z - M) o_z / sum_z 2^(l_z - M).
+template <int DV, typename T, bool LSE>
 __global__ __launch_bounds__(256)
-void merge_partials_kernel(const float* __restrict__ ws, __bf16* __restrict__ out, int64_t rows,
+void merge_partials_kernel(const float* __restrict__ ws, T* __restrict__ out, int64_t rows,
                            int splits) {
   constexpr int Q = DV / 4;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1423,17 +1461,31 @@ void merge_partials_kernel(const float* __restrict__ ws, __bf16* __restrict__ ou
   const float* wd = ws + (int64_t)splits * rows * DV;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int z = 0; z < splits; ++z) {
-    num += *reinterpret_cast<const f32x4*>(ws + ((int64_t)z * rows + row) * DV + 4 * c4);
-    den += wd[(int64_t)z * rows + row];
+  if constexpr (LSE) {
+    float mx = -__builtin_inff();
+    for (int z = 0; z < splits; ++z) mx = __builtin_fmaxf(mx, wd[(int64_t)z * rows + row]);
+    for (int z = 0; z < splits; ++z) {
+      const float wz = __builtin_amdgcn_exp2f(wd[(int64_t)z * rows + row] - mx);
+      num += wz * *reinterpret_cast<const f32x4*>(ws + ((int64_t)z * rows + row) * DV + 4 * c4);
+      den += wz;
+    }
+  } else {
+    for (int z = 0; z < splits; ++z) {
+      num += *reinterpret_cast<const f32x4*>(ws + ((int64_t)z * rows + row) * DV + 4 * c4);
+      den += wd[(int64_t)z * rows + row];
+    }
   }
   const float inv = 1.0f / den;
-  const f32x2 a = {num[0] * inv, num[1] * inv};
-  const f32x2 c = {num[2] * inv, num[3] * inv};
-  u32x2 wv;
-  wv.x = __builtin_bit_cast(unsigned int, __builtin_convertvector(a, bf16x2));
-  wv.y = __builtin_bit_cast(unsigned int, __builtin_convertvector(c, bf16x2));
-  *reinterpret_cast<u32x2*>(out + row * DV + 4 * c4) = wv;
+  if constexpr (sizeof(T) == 2) {
+    const f32x2 a = {num[0] * inv, num[1] * inv};
+    const f32x2 c = {num[2] * inv, num[3] * inv};
+    u32x2 wv;
+    wv.x = __builtin_bit_cast(unsigned int, __builtin_convertvector(a, bf16x2));
+    wv.y = __builtin_bit_cast(unsigned int, __builtin_convertvector(c, bf16x2));
+    *reinterpret_cast<u32x2*>(out + row * DV + 4 * c4) = wv;
+  } else {
+    *reinterpret_cast<f32x4*>(out + row * DV + 4 * c4) = num * inv;
+  }
 }
 
 template <int DV, bool TAIL, bool FUSED>
@@ -1464,7 +1516,7 @@ hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, f
   if (e != hipSuccess) return e;
   const int64_t rows = a.B * a.Sq * kHeads;
   const int64_t threads = rows * (DV / 4);
-  hipLaunchKernelGGL(merge_partials_kernel<DV>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((merge_partials_kernel<DV, __bf16, false>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, a.ws, out, rows, splits);
   return hipGetLastError();
 }
@@ -1498,12 +1550,23 @@ hipError_t launch_typed(const AttnLaunch& a, hipStream_t stream) {
                        : launch_fast<128>(a, stream, alpha, beta_mul, den_a);
   } else {
     const bool tail = a.Sk % kTileKeys != 0 || a.Sq % kBlockPos != 0;
-    dim3 grid((unsigned)((a.Sq + kBlockPos - 1) / kBlockPos), (unsigned)a.B);
-    auto kern = tail ? biased_mqa_fwd_kernel<T, CAPPED, true> : biased_mqa_fwd_kernel<T, CAPPED, false>;
+    const int splits = (int)a.kv_splits;
+    const int tiles = (int)((a.Sk + kTileKeys - 1) / kTileKeys) / splits;
+    dim3 grid((unsigned)((a.Sq + kBlockPos - 1) / kBlockPos), (unsigned)a.B, (unsigned)splits);
+    auto kern = splits > 1 ? (tail ? biased_mqa_fwd_kernel<T, CAPPED, true, true>
+                                   : biased_mqa_fwd_kernel<T, CAPPED, false, true>)
+                           : (tail ? biased_mqa_fwd_kernel<T, CAPPED, true, false>
+                                   : biased_mqa_fwd_kernel<T, CAPPED, false, false>);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.bias,
-                       static_cast<T*>(a.out), (int)a.Sq, (int)a.Sk, (int)a.q_offset,
+                       static_cast<T*>(a.out), a.ws, (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles,
                        a.bias_batch_stride, (int)a.bias_group, alpha, beta_mul, den_a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t threads = a.B * a.Sq * kHeads * (kD / 4);
+    hipLaunchKernelGGL((merge_partials_kernel<kD, T, !CAPPED>), dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, stream, a.ws, static_cast<T*>(a.out), a.B * a.Sq * kHeads,
+                       splits);
     return hipGetLastError();
   }
 }

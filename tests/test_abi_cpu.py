@@ -103,13 +103,15 @@ def attn_ex(**kw):
 
 # Every case must stay invalid: the pointers are not device memory.
 ATTN_EX_CASES = [
-    (dict(Sq=1000, dtype=F32, kv_splits=2), UNSUP), (dict(Sq=0), SHAPE), (dict(Sq=8192 + 32), SHAPE),
+    (dict(Sq=1000, dtype=F32, kv_splits=2, Dv=192), UNSUP), (dict(Sq=0), SHAPE), (dict(Sq=8192 + 32), SHAPE),
     (dict(q_offset=8), UNSUP), (dict(q_offset=-16), SHAPE), (dict(q_offset=8192 - 1024 + 16), SHAPE),
     (dict(kv_splits=0), SHAPE), (dict(kv_splits=65), SHAPE), (dict(kv_splits=3), SHAPE),
-    (dict(dtype=F32), UNSUP), (dict(softcap=0.0), UNSUP),
+    # key ranges on the generic kernel (float32 or no cap): same workspace rules
+    (dict(dtype=F32, ws=None), NULL), (dict(softcap=0.0, ws_bytes=1024), SHAPE),
+    (dict(dtype=F32, kv_splits=3), SHAPE), (dict(softcap=0.0, ws=Q), ALIAS),
     (dict(ws=None), NULL), (dict(ws_bytes=1024), SHAPE), (dict(ws=WS + 8), ALIGN),
     (dict(ws=Q), ALIAS), (dict(ws=OUT - 1024), ALIAS),
-    (dict(Sk=8192 + 64, dtype=F32, kv_splits=3), UNSUP), (dict(Dv=192, dtype=F32, kv_splits=1), UNSUP),
+    (dict(Sk=8192 + 64, dtype=F32, kv_splits=3, ws=None), NULL), (dict(Dv=192, dtype=F32, kv_splits=1), UNSUP),
     # 8192 + 16 keys make 129 tiles, which 8 ranges do not divide
     (dict(Sk=8192 + 16), SHAPE), (dict(Sk=100, Sq=64, q_offset=0, kv_splits=4), SHAPE),
     (dict(q=None), NULL), (dict(out=Q), ALIAS),

@@ -352,6 +352,39 @@ def test_generic_kernel_tails(case):
     print(f"  generic tails {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
 
 
+# Key ranges on the generic kernel: with the cap the ranges share the fixed
+# maximum and their sums add; without it each range keeps its own running
+# maximum and the merge takes the page's update equations across ranges
+# (with bias std 60 the ranges' maxima differ by tens).
+GENERIC_SPLITS = [
+    # dtype, cap, B, S, q_rows (start, stop) or None, kv_splits, bias_std
+    ("f32", 5.0, 2, 512, None, 2, 2.0),
+    ("f32", 5.0, 1, 1000, None, 4, 2.0),
+    ("f32", 0.0, 1, 1000, None, 16, 2.0),        # one tile per range, the last partial
+    ("bf16", 0.0, 2, 777, None, 13, 2.0),        # 13 single-tile ranges, two items
+    ("bf16", 0.0, 1, 1100, (16, 61), 3, 2.0),    # ranges of 6 tiles, 45 queries
+    ("f32", 0.0, 1, 2048, (1024, 1536), 8, 2.0),
+    ("f32", 0.0, 1, 1000, None, 4, 60.0),
+    ("bf16", 0.0, 1, 640, (64, 101), 10, 60.0),
+]
+
+
+@pytest.mark.parametrize("case", GENERIC_SPLITS, ids=lambda c: "%s_cap%g_B%d_S%d_q%s_z%d_b%g" % c)
+def test_generic_kernel_key_ranges(case):
+    dt, cap, B, S, qr, z, bstd = case
+    L = workloads.make_custom(B=B, S=S, dtype=dt, C=16, seed=1700 + S + z, qkv_std=1.0,
+                              bias_std=bstd)
+    L.cap = cap
+    rows = range(0, S) if qr is None else range(*qr)
+    out = _run_ex(L, rows, kv_splits=z)
+    bias64 = _oracle_bias(L)
+    for b in range(B):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, np.arange(rows.start, rows.stop),
+                                    scale=L.scale, cap=cap, batch=b)
+        ok, ma, rel = attention_ok(out[b], ref, dt)
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_attention_long_sampled():
     """S = 65536 (4096 compact cells per side, 1024 key tiles, a 512 MiB
     bias), far past the workloads' lengths: sampled rows, through the

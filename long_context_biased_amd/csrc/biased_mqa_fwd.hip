@@ -25,14 +25,17 @@
 //     keys loaded into A are permuted (bits 2 and 3 of the row swapped; the
 //     permutation is applied when K is staged in LDS) so that each lane's
 //     8-value B fragment covers 8 consecutive keys;
-//   * V is transposed into LDS (V^T, keys contiguous) while it is staged, so
-//     a PV A operand is one 16-byte LDS read per lane;
-//   * LDS rows are padded by 16 bytes (K: 272 B, V^T: 144 B for bf16) so the
-//     32 rows read by a half-wave fall in distinct banks and every fragment
-//     address is one per-lane base plus an immediate offset;
-//   * the compact bias cells of a tile (8 heads x 2 position cells x 4 key
-//     cells) are staged with the tile, pre-multiplied by the exponent-domain
-//     constant; the index (i>>4, j>>4) is fixed per lane and register;
+//   * tiles are staged in LDS in one of two ways.  The generic kernel
+//     (float32, or no cap) stages through registers: V is transposed into
+//     LDS (V^T, keys contiguous) so a PV A operand is one 16-byte LDS read
+//     per lane; LDS rows are padded by 16 bytes (K: 272 B, V^T: 144 B for
+//     bf16) so the 32 rows read by a half-wave fall in distinct banks; the
+//     compact bias cells of a tile (8 heads x 2 position cells x 4 key
+//     cells) are staged with it, pre-multiplied by the exponent-domain
+//     constant, and the index (i>>4, j>>4) is fixed per lane and register.
+//     The bf16 kernel with the cap copies HBM straight to LDS, keeps V
+//     row-major and reads it transposed, and starts each QK^T accumulator
+//     from the tile's bias offsets (see the block comment of that path);
 //   * software pipeline: a 64-key tile is two 32-key halves.  Each stage
 //     issues 16 MFMAs (PV of one half + QK^T of the next tile's half) and,
 //     woven between them, the soft-cap/softmax chain of another half, so the
@@ -44,7 +47,7 @@
 //     apart;
 //   * LDS tiles are triple-buffered for bf16 (one barrier per tile) and
 //     double-buffered for float32 (two barriers per tile, LDS budget); the
-//     global loads of tile t+3 are in flight while tile t computes.
+//     global loads of later tiles are in flight while tile t computes.
 //
 // Soft-capped softmax (cap > 0): since |L| < cap, exp(L - cap) lies in
 // (e^-2cap, 1] and can be used directly: the running maximum of the online

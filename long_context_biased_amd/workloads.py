@@ -211,3 +211,36 @@ def make_custom(*, B: int, S: int, dtype: str, C: int = 16, seed: int = 0,
     return Layer(name="custom", dtype=dtype, q=_cast(q, dtype), k=_cast(k, dtype),
                  v=_cast(v, dtype), pair=_cast(pair, dtype),
                  weight=_cast(weight, dtype), bias_group=B // n_pairs)
+
+
+def lattice_pair(p0: int, p1: int, P: int, C: int, xp=np, device=None):
+    """Rows p0 .. p1 - 1 of a [P, P, C] pair representation on an integer
+    lattice, for lengths whose random inputs would not fit a host: entry
+    (p, r, c) is k / 64 with k = (37 p + 101 r + 29 c + 13 (p r mod 257)
+    + 7 (r c mod 61)) mod 256 - 128, an integer in [-128, 128).
+
+    Integer arithmetic, so numpy (``xp=np``) and torch (``xp=torch``, on
+    ``device``) produce the same float32 values, and every value is exact in
+    bf16.  Returns float32 [p1 - p0, P, C]."""
+    if xp is np:
+        def idx(lo, hi, shape):
+            return np.arange(lo, hi, dtype=np.int64).reshape(shape)
+    else:
+        def idx(lo, hi, shape):
+            return xp.arange(lo, hi, dtype=xp.int64, device=device).reshape(shape)
+    p = idx(p0, p1, (-1, 1, 1))
+    r = idx(0, P, (1, -1, 1))
+    c = idx(0, C, (1, 1, -1))
+    k = (37 * p + 101 * r + 29 * c + 13 * ((p * r) % 257) + 7 * ((r * c) % 61)) % 256 - 128
+    return (k.astype(np.float32) if xp is np else k.to(xp.float32)) / 64.0
+
+
+def make_qkv(*, B: int, S: int, dtype: str, seed: int, qkv_std: float = 1.0):
+    """q [B,S,8,128], k and v [B,S,1,128] ~ N(0, qkv_std^2), drawn in that
+    order from PCG64(seed) in float32 and cast to ``dtype``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    q = rng.standard_normal((B, S, HQ, DK), dtype=f32) * f32(qkv_std)
+    k = rng.standard_normal((B, S, 1, DK), dtype=f32) * f32(qkv_std)
+    v = rng.standard_normal((B, S, 1, DV), dtype=f32) * f32(qkv_std)
+    return _cast(q, dtype), _cast(k, dtype), _cast(v, dtype)

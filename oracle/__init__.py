@@ -17,6 +17,7 @@ from .biased_mqa import (  # noqa: F401
     BIAS_BLOCK,
     as_f64,
     attention,
+    attention_row_given_bias_row,
     attention_rows,
     expand_bias,
     logits,

@@ -144,6 +144,31 @@ def attention_rows(q, k, v, bias, rows, *, scale: float, cap: float,
     return out
 
 
+def attention_row_given_bias_row(q_row, k, v, bias_row, *, scale: float,
+                                 cap: float) -> np.ndarray:
+    """Output of one query position from its compact bias row alone.
+
+    ``q_row`` [Hq, Dk], ``k`` [S, Dk], ``v`` [S, Dv] (float or BF16 bits) and
+    ``bias_row`` [Hq, P], the compact bias row of the query's cell
+    (``bias[h, i // 16, :]``).  The steps of ``attention_rows`` for one
+    position: repeat the row 16 times along the keys, the logit equation,
+    the soft-cap, a two-pass softmax and the weighted sum of V.  It lets a
+    check reach positions of sequences whose whole compact bias would not fit
+    in host memory.  Returns [Hq, Dv].
+    """
+    kb = as_f64(k)
+    vb = as_f64(v)
+    S = kb.shape[0]
+    br = as_f64(bias_row)
+    q_row = np.asarray(q_row)
+    out = np.empty((q_row.shape[0], vb.shape[-1]), dtype=np.float64)
+    for h in range(q_row.shape[0]):
+        dense = np.repeat(br[h][None, :], BIAS_BLOCK, axis=1)[:, :S]
+        L = logits(q_row[h][None, :], kb, dense, scale, cap)
+        out[h] = (softmax_two_pass(L) @ vb)[0]
+    return out
+
+
 def attention(q, k, v, bias, *, scale: float, cap: float, bias_index=None,
               row_block: int = 1024) -> np.ndarray:
     """Full output [B, S, Hq, Dv] in float64.

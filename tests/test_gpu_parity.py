@@ -17,7 +17,7 @@ import oracle
 from gpu_util import sample_rows, to_gpu, to_host, upload
 from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, pair_biased_mqa_fwd, workloads
 from long_context_biased_amd import workspace_bytes as abg_workspace_bytes
-from parity import attention_ok, projection_ok
+from parity import attention_ok, attention_ok_long, projection_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -399,6 +399,51 @@ def test_attention_long_sampled():
     rows = sample_rows(L.S, seed=5)
     _check_rows(L, to_host(one), bias64, rows)
     _check_rows(L, to_host(split), bias64, rows)
+
+
+@pytest.mark.parametrize("dt,cap", [("bf16", 5.0), ("f32", 0.0)])
+def test_maximum_length(dt, cap):
+    """S = 262144, the longest sequence the library takes: P = 16384 compact
+    cells per side, so the bias (8 GiB of float32) and the offsets into it,
+    into K/V and into the output reach their largest values.  The pair
+    representation [16384, 16384, 8] sits on an exact integer lattice (built
+    on the GPU, and row by row on the host for the oracle, from the same
+    integer formula); projection, then attention; sampled rows against the
+    oracle's one-position entry, which needs only each query's bias row."""
+    import time
+    S, C = 262144, 8
+    P = S // 16
+    t0 = time.time()
+    q, k, v = workloads.make_qkv(B=1, S=S, dtype=dt, seed=262144 + (cap > 0), qkv_std=1.0)
+    rng = np.random.Generator(np.random.PCG64(77))
+    w = rng.standard_normal((C, 8), dtype=np.float32) * np.float32(2.0 / math.sqrt(C))
+    w = workloads.f32_to_bf16_bits(w) if dt == "bf16" else w
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    pair = torch.empty((1, P, P, C), dtype=tdt, device="cuda")
+    for p0 in range(0, P, 512):
+        pair[0, p0:p0 + 512] = workloads.lattice_pair(p0, p0 + 512, P, C, xp=torch,
+                                                      device="cuda").to(tdt)
+    print(f"  max length {dt}: inputs ready in {time.time() - t0:.1f} s", flush=True)
+    bias = pair_bias_project(pair, to_gpu(w))
+    del pair
+    out = biased_mqa_fwd(to_gpu(q), to_gpu(k), to_gpu(v), bias, softcap=cap)
+    torch.cuda.synchronize()
+    del bias
+    got = to_host(out)
+    print(f"  max length {dt}: GPU done at {time.time() - t0:.1f} s", flush=True)
+    kf, vf = oracle.as_f64(k[0, :, 0]), oracle.as_f64(v[0, :, 0])
+    rows = sample_rows(S, seed=11)
+    worst = (0.0, 0.0)
+    for i in rows:
+        pair_row = workloads.lattice_pair(i // 16, i // 16 + 1, P, C)
+        bias_row = oracle.project_pair_bias(pair_row, w)[:, 0, :]
+        ref = oracle.attention_row_given_bias_row(q[0, i], kf, vf, bias_row,
+                                                  scale=1 / math.sqrt(128), cap=cap)
+        ok, ma, rel = attention_ok_long(got[0, i], ref, dt, S)
+        assert ok, f"row {i}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+        worst = (max(worst[0], ma), max(worst[1], rel))
+    print(f"  max length {dt}: {len(rows)} rows, worst max-abs {worst[0]:.3g} rel-L2 "
+          f"{worst[1]:.3g} ({time.time() - t0:.1f} s)", flush=True)
 
 
 def test_single_key_returns_its_value():

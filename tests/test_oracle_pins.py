@@ -57,6 +57,23 @@ def test_attention_rows_matches_full():
     assert np.allclose(part, brute, rtol=0, atol=1e-12)
 
 
+def test_row_given_bias_row_matches_brute_force():
+    """The one-position entry (the query's compact bias row only, for
+    sequences whose whole bias does not fit on the host) against the scalar
+    brute force, on a length off the 16-position cell, with and without the
+    cap, BF16 inputs included."""
+    for seed, S, cap, bf16 in ((610, 37, 5.0, False), (611, 64, 0.0, False), (612, 50, 2.0, True)):
+        q, k, v, bias = pins._rand_case(seed, B=1, S=S, Hq=3, Dk=4, Dv=5, bias_std=2.0)
+        if bf16:
+            from long_context_biased_amd.workloads import f32_to_bf16_bits
+            q, k, v = (f32_to_bf16_bits(np.asarray(x, dtype=np.float32)) for x in (q, k, v))
+        brute = np.array(oracle.attention_brute(q, k, v, bias, scale=0.5, cap=cap))[0]
+        for i in (0, 15, 16, S - 1):
+            row = oracle.attention_row_given_bias_row(q[0, i], k[0, :, 0], v[0, :, 0],
+                                                      bias[0][:, i // 16, :], scale=0.5, cap=cap)
+            assert np.allclose(row, brute[i], rtol=0, atol=1e-12), (seed, i)
+
+
 def test_bf16_decoding_is_exact():
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F, 0x3C00], dtype=np.uint16)
     vals = oracle.as_f64(bits)

@@ -1017,17 +1017,34 @@ __device__ __forceinline__ float sum8(float x) {
 //
 // From copied compact-bias cells: lane l writes entry l of the head's 64
 // (hf = l >> 5, qc = (l >> 4) & 1, key cell 2 hf + ((l >> 3) & 1)).
+// The read and the write are separate calls so that the loop can issue the
+// read before a stage and the write after it: read right before its use, the
+// cell would make the wave wait for every LDS read in flight, the ring's
+// prefetches included.
 template <int HPW, int DV, int S>
-__device__ __forceinline__ void expand_bias(char* smem, int wave, float beta_mul) {
+__device__ __forceinline__ void bias_cells_load(const char* smem, int wave, float (&b)[HPW]) {
   using L = FP<DV>;
   const int lane = (int)threadIdx.x & 63;
   const int cell = ((lane >> 4) & 1) * 4 + 2 * (lane >> 5) + ((lane >> 3) & 1);
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const int h = wave * HPW + hh;
-    const float b = reinterpret_cast<const float*>(smem + L::B0 + S * 256)[h * 8 + cell];
-    reinterpret_cast<float*>(smem + L::XB0 + S * L::XBS)[h * 64 + lane] = b * beta_mul;
-  }
+  for (int hh = 0; hh < HPW; ++hh)
+    b[hh] = reinterpret_cast<const float*>(smem + L::B0 + S * 256)[(wave * HPW + hh) * 8 + cell];
+}
+template <int HPW, int DV, int S>
+__device__ __forceinline__ void expand_bias_store(char* smem, int wave, float beta_mul,
+                                                  const float (&b)[HPW]) {
+  using L = FP<DV>;
+  const int lane = (int)threadIdx.x & 63;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    reinterpret_cast<float*>(smem + L::XB0 + S * L::XBS)[(wave * HPW + hh) * 64 + lane] =
+        b[hh] * beta_mul;
+}
+template <int HPW, int DV, int S>
+__device__ __forceinline__ void expand_bias(char* smem, int wave, float beta_mul) {
+  float b[HPW];
+  bias_cells_load<HPW, DV, S>(smem, wave, b);
+  expand_bias_store<HPW, DV, S>(smem, wave, beta_mul, b);
 }
 
 // Projected from the pair vectors (FUSED).  Cell (qc, kc) of head h is
@@ -1080,15 +1097,18 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUS
   issue_kv<HPW, DV, TAIL, FUSED, NN>(smem, c, min(t + 2, last));
   issue_cells<HPW, DV, TAIL, FUSED, C>(smem, c, min(t + 3, last));
   // pair vectors of tile t+2: read during X (value width 128), or after it
-  // (192, whose stage leaves no registers for them)
+  // (192, whose stage leaves no registers for them); its compact-bias cells
+  // are read during X as well
   bf16x8 pv[2];
+  float bc[HPW];
   if constexpr (FUSED && DV == 128) pair_load<DV, NN>(smem, pv);
+  if constexpr (!FUSED) bias_cells_load<HPW, DV, NN>(smem, c.wave, bc);
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
   fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, P1, ring);
   if constexpr (FUSED && DV != 128) pair_load<DV, NN>(smem, pv);
   // the exponent offsets of tile t+2, read by the next iteration
   if constexpr (FUSED) pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
-  else expand_bias<HPW, DV, NN>(smem, c.wave, c.beta_mul);
+  else expand_bias_store<HPW, DV, NN>(smem, c.wave, c.beta_mul, bc);
   // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
   fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, P0, ring);
   tile_barrier();

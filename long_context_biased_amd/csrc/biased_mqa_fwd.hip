@@ -825,6 +825,71 @@ __device__ __forceinline__ f32x16 beta_acc(const char* smem, const int (&xbl)[HP
   return *reinterpret_cast<const f32x16*>(smem + xbl[hh] + S * FP<DV>::XBS + KB * 128);
 }
 
+// x plus the value x holds in the lane that the DPP control CTRL names
+// (within each row of 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                  0xF, 0xF, false));
+}
+// Sum over each group of 8 lanes (every lane of the group gets the same sum:
+// each step adds the same two values in either order): quad_perm 1,0,3,2,
+// quad_perm 2,3,0,1, row_half_mirror.
+__device__ __forceinline__ float sum8(float x) { return dpp_add<0x141>(dpp_add<0x4E>(dpp_add<0xB1>(x))); }
+
+// Expanded-offset entry (float index within a head's 64) that lane l writes
+// for the cell of pair vector l >> 3 = 4 qc + kc: copy l & 7 of the 8 copies
+// of key cell kc in the half kc >> 1, query cell qc.
+__device__ __forceinline__ int pair_entry(int lane) {
+  const int v = lane >> 3, qc = v >> 2, kc = v & 3;
+  return (kc >> 1) * 32 + qc * 16 + (kc & 1) * 8 + (lane & 7);
+}
+
+// The projection of the next tile's bias cells (pair form), woven into a
+// stage as one VALU micro-op per slot: slots 0..7 the dot products (two
+// chains), 8 their sum, 9..11 the sum over the 8 lanes of a vector, 12 the
+// scale and the store of the expanded entry.  Same operations, in the same
+// order, as pair_store, whose dependent chain would otherwise stall the wave
+// between two stages.
+template <int HPW>
+struct ProjIn {
+  const bf16x8* pv;           // [2] this lane's pair channels
+  const uint32_t (*wreg)[8];  // [HPW][8] projection weights
+  float beta_mul;
+  float* dst[HPW];            // this lane's expanded entry, per head
+};
+struct ProjState {
+  float s0, s1, t;
+};
+template <int HPW>
+__device__ __forceinline__ void proj_op(int j, const ProjIn<HPW>& in, ProjState& st, int hh) {
+  if (j < 8) {
+    const bf16x2 w = __builtin_bit_cast(bf16x2, in.wreg[hh][j]);
+    const bf16x2 x = {in.pv[j >> 2][2 * (j & 3)], in.pv[j >> 2][2 * (j & 3) + 1]};
+    if (j & 1) st.s1 = __builtin_amdgcn_fdot2_f32_bf16(x, w, st.s1, false);
+    else st.s0 = __builtin_amdgcn_fdot2_f32_bf16(x, w, st.s0, false);
+  } else if (j == 8) {
+    st.t = st.s0 + st.s1;
+  } else if (j == 9) {
+    st.t = dpp_add<0xB1>(st.t);
+  } else if (j == 10) {
+    st.t = dpp_add<0x4E>(st.t);
+  } else if (j == 11) {
+    st.t = dpp_add<0x141>(st.t);
+  } else if (j == 12) {
+    *in.dst[hh] = st.t * in.beta_mul;
+  }
+}
+// A scheduling group of n VALU instructions (the builtin takes its count as
+// a constant; n is a constant once the slot loop is unrolled).
+template <int N>
+__device__ __forceinline__ void valu_group() { __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, N, 0); }
+__device__ __forceinline__ void valu_group_n(int n) {
+  if (n == 4) valu_group<4>(); else if (n == 5) valu_group<5>(); else if (n == 6) valu_group<6>();
+  else if (n == 7) valu_group<7>(); else if (n == 8) valu_group<8>(); else if (n == 10) valu_group<10>();
+  else if (n == 12) valu_group<12>(); else valu_group<14>();
+}
+
 // One stage: for each of the HPW heads of the wave, 8 + 2 DV/32 MFMAs (PV of
 // half KB of the tile in V stage SV, QK^T of half KB of the tile in K stage
 // SK, its accumulator started from that half's exponent offsets) woven with
@@ -832,16 +897,20 @@ __device__ __forceinline__ f32x16 beta_acc(const char* smem, const int (&xbl)[HP
 // LDS feeds the MFMAs of all HPW heads.  ring[] holds A fragments three
 // slots ahead; the last three slots fetch the first three fragments of the
 // following stage (PV on half NKB of V stage NSV).
-template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB>
+template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB, bool PROJ = false>
 __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
                                        const int (&vro)[DV / 32], const int (&xbl)[HPW],
                                        const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][DV / 32],
                                        f32x16 (&sout)[HPW], const bf16x8 (&pin)[HPW][2],
                                        const f32x16 (&ssm)[HPW], float den_a, float (&rowsum)[HPW],
-                                       bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4]) {
+                                       bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4],
+                                       const ProjIn<HPW>* proj = nullptr) {
   constexpr int NPV = DV / 32;
   constexpr int NSLOT = 8 + 2 * NPV;
   SmState sm[HPW];
+  ProjState pst[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) pst[hh] = ProjState{0.f, 0.f, 0.f};
   f32x16 acc[HPW];  // QK^T of the next half starts from its exponent offsets
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) acc[hh] = beta_acc<HPW, SK, KB, DV>(smem, xbl, hh);
@@ -865,14 +934,13 @@ __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
       for (int u = 0; u < sm_count<NSLOT>(j); ++u)
         sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh],
               ssm[hh], den_a, rowsum[hh]);
+      if constexpr (PROJ) proj_op<HPW>(j, *proj, pst[hh], hh);
     }
     // inside the slot: the MFMA first, then the LDS reads, then the VALU work
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    if (sm_count<NSLOT>(j) == 6) __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6 * HPW, 0);
-    else if (sm_count<NSLOT>(j) == 5) __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 5 * HPW, 0);
-    else __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 4 * HPW, 0);
+    valu_group_n((sm_count<NSLOT>(j) + (PROJ && j <= 12 ? 1 : 0)) * HPW);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -998,14 +1066,6 @@ __device__ __forceinline__ void tile_barrier() {
   __syncthreads();
 }
 
-// Sum over each group of 8 lanes (every lane of the group gets the same
-// sum: each step adds the same two values in either order).
-__device__ __forceinline__ float sum8(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)); // row_half_mirror
-  return x;
-}
 
 // Exponent offsets of the tile in slot S for the wave's heads: beta = bias
 // cell x the exponent factor, written expanded to the accumulator layout of
@@ -1064,9 +1124,7 @@ template <int HPW, int DV, int S>
 __device__ __forceinline__ void pair_store(char* smem, const bf16x8 (&a)[2], const uint32_t (&wreg)[HPW][8],
                                            int wave, float beta_mul) {
   using L = FP<DV>;
-  const int lane = (int)threadIdx.x & 63;
-  const int v = lane >> 3, qc = v >> 2, kc = v & 3;
-  const int entry = (kc >> 1) * 32 + qc * 16 + (kc & 1) * 8 + (lane & 7);
+  const int entry = pair_entry((int)threadIdx.x & 63);
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     float s[2] = {0.f, 0.f};  // two chains, added at the end
@@ -1107,10 +1165,24 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUS
   fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, P1, ring);
   if constexpr (FUSED && DV != 128) pair_load<DV, NN>(smem, pv);
   // the exponent offsets of tile t+2, read by the next iteration
-  if constexpr (FUSED) pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
-  else expand_bias_store<HPW, DV, NN>(smem, c.wave, c.beta_mul, bc);
+  if constexpr (FUSED && DV != 128) pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
+  if constexpr (!FUSED) expand_bias_store<HPW, DV, NN>(smem, c.wave, c.beta_mul, bc);
   // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
-  fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, P0, ring);
+  if constexpr (FUSED && DV == 128) {
+    // value width 128: the projection of tile t+2 woven into stage Y
+    ProjIn<HPW> pj;
+    pj.pv = pv;
+    pj.wreg = c.wreg;
+    pj.beta_mul = c.beta_mul;
+    const int entry = pair_entry((int)threadIdx.x & 63);
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+      pj.dst[hh] = reinterpret_cast<float*>(smem + FP<DV>::XB0 + NN * FP<DV>::XBS) +
+                   (c.wave * HPW + hh) * 64 + entry;
+    fstage<HPW, DV, C, NXT, 1, NXT, 0, true>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, P0, ring, &pj);
+  } else {
+    fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, P0, ring);
+  }
   tile_barrier();
 }
 

@@ -1111,7 +1111,7 @@ __device__ __forceinline__ void expand_bias(char* smem, int wave, float beta_mul
 // sum_c pair[qc, kc, c] W[c, h] (bf16 products, float32 sums).  Lane l holds
 // channels 16 (l & 7) .. + 15 of pair vector l >> 3 = 4 qc + kc (pair_load);
 // the 8 lanes of a vector sum it, and lane l & 7 writes copy l & 7 of the
-// cell's 8 (pair_store).
+// cell's 8 (pair_store between two stages, or proj_op woven into one).
 template <int DV, int S>
 __device__ __forceinline__ void pair_load(const char* smem, bf16x8 (&a)[2]) {
   using L = FP<DV>;

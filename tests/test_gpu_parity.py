@@ -78,6 +78,29 @@ def test_projection_small_shapes():
         assert ok, f"case {seed}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
+@pytest.mark.parametrize("P,C", [(4096, 32), (2400, 128)])
+def test_projection_many_steps(P, C):
+    """Grids past the launch cap, so that every wave of the matrix-core
+    projection kernel takes several 16-cell steps through its LDS slice:
+    a pair representation on the exact integer lattice (built on the GPU;
+    the oracle rebuilds the sampled rows on the host from the same formula),
+    sampled rows against the oracle."""
+    pair = torch.empty((1, P, P, C), dtype=torch.bfloat16, device="cuda")
+    for p0 in range(0, P, 256):
+        p1 = min(P, p0 + 256)
+        pair[0, p0:p1] = workloads.lattice_pair(p0, p1, P, C, xp=torch, device="cuda").to(torch.bfloat16)
+    rng = np.random.Generator(np.random.PCG64(P + C))
+    w = workloads.f32_to_bf16_bits(rng.standard_normal((C, 8), dtype=np.float32) *
+                                   np.float32(1.0 / math.sqrt(C)))
+    got = pair_bias_project(pair, to_gpu(w))
+    torch.cuda.synchronize()
+    del pair
+    for row in (0, 1, 777, P // 2, P - 2, P - 1):
+        ref = oracle.project_pair_bias(workloads.lattice_pair(row, row + 1, P, C), w)[:, 0, :]
+        ok, ma, rel = projection_ok(to_host(got[0, :, row, :]), ref)
+        assert ok, f"row {row}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 # ---------------------------------------------------------------------------
 # Attention: every output at small and medium sizes
 # ---------------------------------------------------------------------------

@@ -469,6 +469,30 @@ def test_maximum_length(dt, cap):
           f"{worst[1]:.3g} ({time.time() - t0:.1f} s)", flush=True)
 
 
+@pytest.mark.parametrize("route", ["bias", "pair"])
+def test_maximum_batch(route):
+    """B = 65535, the most batch items the ABI takes (the grid's second
+    dimension), each with its own bias or pair block, S = 3: sampled items
+    against the oracle, the last one included."""
+    B, S = 65535, 3
+    L = workloads.make_custom(B=B, S=S, dtype="bf16", C=128 if route == "pair" else 8, seed=65535,
+                              qkv_std=1.0, bias_std=2.0)
+    t = upload(L)
+    if route == "pair":
+        out = pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], scale=L.scale,
+                                  softcap=L.cap)
+    else:
+        bias = pair_bias_project(t["pair"], t["weight"])
+        out = biased_mqa_fwd(t["q"], t["k"], t["v"], bias, scale=L.scale, softcap=L.cap)
+    torch.cuda.synchronize()
+    bias64 = _oracle_bias(L)
+    for b in (0, 1, 4097, 40000, B - 1):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, np.arange(S), scale=L.scale, cap=L.cap,
+                                    batch=b)
+        ok, ma, rel = attention_ok(to_host(out[b]), ref, "bf16")
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_single_key_returns_its_value():
     """S = 1: every query attends to the one key with weight 1, so the output
     is that key's value row (rounded to bf16 it is exact)."""

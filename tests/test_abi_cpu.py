@@ -257,3 +257,15 @@ def test_plain_c_consumer(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     assert "c consumer ok" in r.stdout
+
+
+def test_build_flags():
+    """Every HIP source is compiled for gfx950 with packed FP32 VALU
+    instructions disabled (the compiler would otherwise form them from
+    ordinary float code)."""
+    from long_context_biased_amd import _build
+    f = _build.HIP_FLAGS
+    assert "--offload-arch=gfx950" in f
+    i = f.index("-packed-fp32-ops")
+    assert f[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
+    assert set(_build.SOURCES) == {"biased_mqa_fwd.hip", "pair_bias_project.hip", "abg_api.cpp"}

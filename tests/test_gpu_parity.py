@@ -702,13 +702,18 @@ def test_deterministic_and_stream_ordered():
 def test_graph_capture_replays():
     """The calls capture into a HIP graph (through torch.cuda.graph) and every
     replay equals the eager result bit for bit: the plain call, key ranges
-    with a caller-owned workspace, and the pair form.  Eager work runs
-    between the replays, and each replay is checked on its own."""
+    with a caller-owned workspace, the pair form, and the generic kernel
+    (float32, no cap) with key ranges.  Eager work runs between the
+    replays, and each replay is checked on its own."""
     L = workloads.make_custom(B=1, S=1000, dtype="bf16", C=128, seed=77, qkv_std=1.0, bias_std=2.0)
     t = upload(L)
     bias = pair_bias_project(t["pair"], t["weight"])
     ws = torch.empty(abg_workspace_bytes(1, 1000, 8, 128, 4), dtype=torch.uint8, device="cuda")
-    outs = [torch.empty_like(t["q"]) for _ in range(3)]
+    F = workloads.make_custom(B=1, S=1000, dtype="f32", C=16, seed=78, qkv_std=1.0, bias_std=2.0)
+    tf = upload(F)
+    fbias = pair_bias_project(tf["pair"], tf["weight"])
+    ws2 = torch.empty(abg_workspace_bytes(1, 1000, 8, 128, 4), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(t["q"]) for _ in range(3)] + [torch.empty_like(tf["q"])]
 
     def calls():
         biased_mqa_fwd(t["q"], t["k"], t["v"], bias, outs[0], scale=L.scale, softcap=L.cap)
@@ -716,6 +721,8 @@ def test_graph_capture_replays():
                        kv_splits=4, workspace=ws)
         pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], outs[2],
                             scale=L.scale, softcap=L.cap)
+        biased_mqa_fwd(tf["q"], tf["k"], tf["v"], fbias, outs[3], scale=F.scale, softcap=0.0,
+                       kv_splits=4, workspace=ws2)
 
     calls()
     torch.cuda.synchronize()

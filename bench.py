@@ -42,6 +42,7 @@ import numpy as np  # noqa: E402
 
 #: MI355X published dense peaks used for the roofline.
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "biased_mqa_fwd_full_counters.txt")
 
@@ -140,6 +141,53 @@ def cpu_baseline(host_layers):
                        f"8 heads each), float64 numpy, {dt:.1f} s wall; BLAS threads = cores")}
 
 
+def attention_only(args, torch, dev, biased_mqa_fwd, workloads):
+    """One attention kernel, B = 1, S = --seq-len, a random compact bias:
+    K launches back to back between two events after the clock settles.
+    Prints one JSON line (not the headline metric)."""
+    dt, cap = args.attention_only.split(":")
+    cap = float(cap)
+    S = args.seq_len
+    L = workloads.make_custom(B=1, S=S, dtype=dt, C=8, seed=S, qkv_std=1.0, bias_std=2.0)
+
+    def g(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = g(L.q), g(L.k), g(L.v)
+    P = -(-S // 16)
+    bias = torch.randn(8, P, P, device=dev, generator=torch.Generator(device=dev).manual_seed(S))
+    out = torch.empty_like(q)
+    t_end = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        biased_mqa_fwd(q, k, v, bias, out, softcap=cap)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        biased_mqa_fwd(q, k, v, bias, out, softcap=cap)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        biased_mqa_fwd(q, k, v, bias, out, softcap=cap)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    fl = attn_flops(1, S)
+    tf = fl / (us * 1e-6) / 1e12
+    peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_FP32_MATRIX_TFLOPS
+    kernel = ("biased_mqa_fwd_bf16_capped_kernel" if (dt == "bf16" and cap > 0) else
+              "biased_mqa_fwd_kernel (generic)")
+    log(f"attention only, {dt}, cap {cap:g}, S={S}: {us:.1f} us per launch = {tf:.1f} TFLOP/s")
+    print(json.dumps({"metric": f"attention kernel TFLOP/s, {dt}, cap {cap:g}, S={S}, 8 heads, "
+                                f"d=128", "value": round(tf, 2), "unit": "TFLOP/s",
+                      "avg_launch_us": round(us, 2), "steps": args.steps,
+                      "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
+                                   "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                                   "kernel": kernel, "flops_per_launch": fl}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +215,13 @@ def main():
     ap.add_argument("--path", default=None, choices=("pair", "two"),
                     help="pair (default): the projection inside the attention kernel; two: "
                          "projection kernel + attention kernel")
+    ap.add_argument("--attention-only", default=None,
+                    choices=("bf16:5", "bf16:0", "f32:5", "f32:0"),
+                    help="instead of the headline step, time the attention kernel alone for "
+                         "this dtype and cap (0 = uncapped: the generic kernel) on one layer "
+                         "of --seq-len positions, against the matching matrix-core peak")
+    ap.add_argument("--seq-len", type=int, default=8192,
+                    help="sequence length for --attention-only")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the measurement, run 3 plain device-to-device copies of this "
                          "many MiB (a known-size reference for HBM byte counters)")
@@ -187,6 +242,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     n_layers = args.layers
+    if args.attention_only:
+        attention_only(args, torch, dev, biased_mqa_fwd, workloads)
+        return
 
     def to_gpu(a):
         a = np.ascontiguousarray(a)

@@ -15,7 +15,7 @@ struct AttnLaunch {
   const void* v;
   const float* bias;          // compact bias, or NULL when pair is given
   const void* pair;           // bf16 pair representation [., P, P, 128] whose
-                              // projection replaces bias (bf16, cap, Dv 128)
+                              // projection replaces bias (bf16 with the cap)
   const void* weight;         // bf16 [128, 8] projection weight with pair
   void* out;
   float* ws;                  // fp32 partials when kv_splits > 1, else unused

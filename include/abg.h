@@ -129,7 +129,8 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
 
 /* Workspace bytes that abg_biased_mqa_fwd_ex needs for kv_splits key ranges:
  * 0 for kv_splits == 1, else kv_splits * B * Sq * Hq * (Dv + 1) * 4 (float32
- * partial numerators and denominators).  -1 for out-of-range arguments. */
+ * partial numerators and denominators).  -1 for out-of-range arguments
+ * (any below 1, kv_splits above 64, or a size past INT64_MAX). */
 int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
                                            int64_t kv_splits);
 

@@ -216,7 +216,12 @@ int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, in
                                            int64_t kv_splits) {
   if (B < 1 || Sq < 1 || Hq < 1 || Dv < 1 || kv_splits < 1 || kv_splits > 64) return -1;
   if (kv_splits == 1) return 0;
-  return kv_splits * B * Sq * Hq * (Dv + 1) * 4;
+  // a product past int64 is out of range as well
+  int64_t n = kv_splits;
+  const int64_t f[5] = {B, Sq, Hq, Dv + 1, 4};
+  for (int64_t x : f)
+    if (__builtin_mul_overflow(n, x, &n)) return -1;
+  return n;
 }
 
 abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,

@@ -168,7 +168,8 @@ def test_workspace_bytes():
     assert abg.workspace_bytes(1, 2048, 8, 128, 1) == 0
     assert abg.workspace_bytes(2, 1024, 8, 128, 4) == 4 * 2 * 1024 * 8 * 129 * 4
     assert abg.workspace_bytes(1, 1024, 8, 192, 8) == 8 * 1024 * 8 * 193 * 4
-    for bad in [(0, 1024, 8, 128, 2), (1, 1024, 8, 128, 0), (1, 1024, 8, 128, 65)]:
+    for bad in [(0, 1024, 8, 128, 2), (1, 1024, 8, 128, 0), (1, 1024, 8, 128, 65),
+                (2**40, 2**20, 8, 128, 64), (1, 2**62, 8, 128, 2)]:
         assert abg.workspace_bytes(*bad) == -1
     assert abg.auto_kv_splits(1, 2048, 2048) == 4
     assert abg.auto_kv_splits(1, 8192, 8192) == 1

@@ -227,7 +227,7 @@ def main():
                          "many MiB (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

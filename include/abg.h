@@ -49,7 +49,7 @@ typedef enum abg_status {
   ABG_OK = 0,
   ABG_ERR_NULL = 1,        /* a required pointer is NULL                         */
   ABG_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent   */
-  ABG_ERR_UNSUPPORTED = 3, /* valid request that this build does not implement   */
+  ABG_ERR_UNSUPPORTED = 3, /* valid request that this library does not implement */
   ABG_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
   ABG_ERR_VALUE = 5,       /* a scalar argument is not finite or out of range    */
   ABG_ERR_ALIAS = 6,       /* the output overlaps an input                       */

@@ -177,8 +177,8 @@ def attention_only(args, torch, dev, biased_mqa_fwd, workloads):
     fl = attn_flops(1, S)
     tf = fl / (us * 1e-6) / 1e12
     peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_FP32_MATRIX_TFLOPS
-    kernel = ("biased_mqa_fwd_bf16_capped_kernel" if (dt == "bf16" and cap > 0) else
-              "biased_mqa_fwd_kernel (generic)")
+    kernel = ("biased_mqa_fwd_kernel (generic, float32)" if dt != "bf16" else
+              "biased_mqa_fwd_bf16_capped_kernel" if cap > 0 else "biased_mqa_fwd_bf16_uncapped_kernel")
     log(f"attention only, {dt}, cap {cap:g}, S={S}: {us:.1f} us per launch = {tf:.1f} TFLOP/s")
     print(json.dumps({"metric": f"attention kernel TFLOP/s, {dt}, cap {cap:g}, S={S}, 8 heads, "
                                 f"d=128", "value": round(tf, 2), "unit": "TFLOP/s",

@@ -26,23 +26,23 @@
 //     permutation is applied when K is staged in LDS) so that each lane's
 //     8-value B fragment covers 8 consecutive keys;
 //   * tiles are staged in LDS in one of two ways.  The generic kernel
-//     (float32, or no cap) stages through registers: V is transposed into
+//     (float32) stages through registers: V is transposed into
 //     LDS (V^T, keys contiguous) so a PV A operand is one 16-byte LDS read
 //     per lane; LDS rows are padded by 16 bytes (K: 272 B, V^T: 144 B for
 //     bf16) so the 32 rows read by a half-wave fall in distinct banks; the
 //     compact bias cells of a tile (8 heads x 2 position cells x 4 key
 //     cells) are staged with it, pre-multiplied by the exponent-domain
 //     constant, and the index (i>>4, j>>4) is fixed per lane and register.
-//     The bf16 kernel with the cap copies HBM straight to LDS, keeps V
+//     The bf16 kernel (with or without the cap) copies HBM straight to LDS, keeps V
 //     row-major and reads it transposed, and starts each QK^T accumulator
 //     from the tile's bias offsets (see the block comment of that path);
 //   * software pipeline: a 64-key tile is two 32-key halves.  Each stage
 //     issues 16 MFMAs (PV of one half + QK^T of the next tile's half) and,
 //     woven between them, the soft-cap/softmax chain of another half, so the
 //     matrix cores and the VALU work at the same time inside one wave; the
-//     second wave on the SIMD fills the remaining gaps.  For bf16 with the
-//     cap the order is fixed by hand: 16 slots of {LDS read three MFMAs
-//     ahead, one MFMA, five softmax micro-ops}, the softmax written as a
+//     second wave on the SIMD fills the remaining gaps.  For bf16 the
+//     order is fixed by hand: 16 slots of {LDS read three MFMAs ahead, one
+//     MFMA, five softmax micro-ops (three without the cap)}, the softmax written as a
 //     skewed pipeline over its 16 values so dependent operations are far
 //     apart;
 //   * LDS tiles are triple-buffered for bf16 (one barrier per tile) and
@@ -55,8 +55,10 @@
 // invariance of softmax and needs no rescaling.  With y = exp(2x/cap),
 //   exp(L - cap) = exp(-2 cap / (1 + y))
 // which costs exp2, fma, rcp, exp2 per logit with every constant folded.
-// Without the cap the kernel keeps the running maximum and rescales (m, d, n)
-// per 32-key half exactly as in the update equations of the page.
+// Without the cap the kernels keep the running maximum of the update
+// equations of the page: the generic kernel rescales (m, d, n) per 32-key
+// half; the bf16 kernel moves its reference maximum only when a row
+// outgrows it by 2^8 (update_ref).
 // The row sum adds the probabilities as rounded for the PV product.
 
 #include <hip/hip_runtime.h>
@@ -404,14 +406,21 @@ __device__ __forceinline__ void softmax_half(const f32x16& s, f32x2 beta, float 
 // done.
 // ---------------------------------------------------------------------------
 struct SmOp { int pass, idx; };
-constexpr int kSmOps = 80;  // 16 values x 4 passes + 8 packs + 8 sums
-struct SmTable { SmOp op[kSmOps]; };
-constexpr SmTable make_sm_table() {
-  SmTable t{};
+// NP arithmetic passes per value (with the cap 4: exp2, fma, rcp, exp2;
+// without it 2: subtract the reference maximum, exp2), then 8 packs and 8
+// sums: 16 NP + 16 micro-ops.
+template <int NP>
+struct SmTable {
+  static constexpr int N = 16 * NP + 16;
+  SmOp op[N];
+};
+template <int NP>
+constexpr SmTable<NP> make_sm_table() {
+  SmTable<NP> t{};
   int n = 0;
-  constexpr int lag = 3, fe = 3 * lag + 3;
-  for (int tau = 0; n < kSmOps; ++tau) {
-    for (int p = 1; p < 5; ++p) {
+  constexpr int lag = 3, fe = (NP - 1) * lag + 3;
+  for (int tau = 0; n < SmTable<NP>::N; ++tau) {
+    for (int p = 1; p <= NP; ++p) {
       const int x = tau - (p - 1) * lag;
       if (x >= 0 && x < 16) t.op[n++] = SmOp{p, x};
     }
@@ -421,7 +430,10 @@ constexpr SmTable make_sm_table() {
   }
   return t;
 }
-constexpr SmTable kSm = make_sm_table();
+constexpr SmTable<4> kSm = make_sm_table<4>();
+constexpr SmTable<2> kSmU = make_sm_table<2>();
+constexpr int kSmOps = SmTable<4>::N;   // 80
+constexpr int kSmOpsU = SmTable<2>::N;  // 48
 
 struct SmState {
   float v[16];
@@ -757,6 +769,48 @@ struct FP {
 };
 
 // MFMA order inside a stage (NPV = DV / 32 blocks of value channels):
+// The same without the cap: pass 1 subtracts the row's reference maximum
+// (base-2 exponents), pass 2 takes exp2; packs and sums as above.
+__device__ __forceinline__ void sm_op_u(int pass, int x, SmState& st, const f32x16& s, float mref,
+                                        float& rowsum) {
+  switch (pass) {
+    case 1: st.v[x] = s[x] - mref; break;
+    case 2: st.v[x] = __builtin_amdgcn_exp2f(st.v[x]); break;
+    case 5: {
+      const f32x2 two = {st.v[2 * x], st.v[2 * x + 1]};
+      st.pk[x] = __builtin_convertvector(two, bf16x2);
+      break;
+    }
+    default: {
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      rowsum = __builtin_amdgcn_fdot2_f32_bf16(st.pk[x], ones, rowsum, false);
+      break;
+    }
+  }
+}
+
+// Running maximum without the cap (the page's online update, base 2): the
+// maximum of a row over the 32 keys of a half (16 exponents in this lane,
+// 16 in lane l ^ 32).  The reference moves only when some row of the wave
+// exceeds it by more than 8, so weights stay below 2^8 (exact enough in
+// bf16, far from overflow) and the accumulators are rescaled rarely; f is
+// the factor for what was accumulated against the old reference (1 when it
+// stays).  Returns whether the wave moved its reference (uniform).
+__device__ __forceinline__ bool update_ref(const f32x16& s, float& mref, float& f) {
+  const float a0 = fmaxf(fmaxf(s[0], s[1]), s[2]), a1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float a2 = fmaxf(fmaxf(s[6], s[7]), s[8]), a3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float a4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  const float m = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[15]));
+  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, m),
+                                                   __builtin_bit_cast(unsigned, m), false, false);
+  const float mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+  const bool any = __builtin_amdgcn_ballot_w64(mh > mref + 8.f) != 0;
+  const float mn = any ? fmaxf(mref, mh) : mref;
+  f = __builtin_amdgcn_exp2f(mref - mn);
+  mref = mn;
+  return any;
+}
+
 // PV(db 0..2, half 0), QK(kc 0..7), PV(db 3..NPV-1, half 0), PV(db 0..NPV-1,
 // half 1) -- 8 + 2 NPV slots.  The QK^T chain ends mid-stage, long before the
 // next stage's softmax reads it, and the first three MFMAs read V only.
@@ -770,13 +824,13 @@ template <int NPV>
 __device__ __forceinline__ constexpr int slot_half(int j) { return j < 8 + NPV ? 0 : 1; }
 // The softmax micro-ops of a stage spread over its slots: as evenly as
 // possible, the first slots taking one more.
-template <int NSLOT>
+template <int NSLOT, int NOPS = kSmOps>
 __device__ __forceinline__ constexpr int sm_count(int j) {
-  return kSmOps / NSLOT + (j < kSmOps % NSLOT ? 1 : 0);
+  return NOPS / NSLOT + (j < NOPS % NSLOT ? 1 : 0);
 }
-template <int NSLOT>
+template <int NSLOT, int NOPS = kSmOps>
 __device__ __forceinline__ constexpr int sm_begin(int j) {
-  return j * (kSmOps / NSLOT) + (j < kSmOps % NSLOT ? j : kSmOps % NSLOT);
+  return j * (NOPS / NSLOT) + (j < NOPS % NSLOT ? j : NOPS % NSLOT);
 }
 
 // V rows in LDS are row-major as in HBM, in 32-byte slots (16 channels)
@@ -885,7 +939,7 @@ __device__ __forceinline__ void proj_op(int j, const ProjIn<HPW>& in, ProjState&
 template <int N>
 __device__ __forceinline__ void valu_group() { __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, N, 0); }
 __device__ __forceinline__ void valu_group_n(int n) {
-  if (n == 4) valu_group<4>(); else if (n == 5) valu_group<5>(); else if (n == 6) valu_group<6>();
+  if (n == 3) valu_group<3>(); else if (n == 4) valu_group<4>(); else if (n == 5) valu_group<5>(); else if (n == 6) valu_group<6>();
   else if (n == 7) valu_group<7>(); else if (n == 8) valu_group<8>(); else if (n == 10) valu_group<10>();
   else if (n == 12) valu_group<12>(); else valu_group<14>();
 }
@@ -897,17 +951,30 @@ __device__ __forceinline__ void valu_group_n(int n) {
 // LDS feeds the MFMAs of all HPW heads.  ring[] holds A fragments three
 // slots ahead; the last three slots fetch the first three fragments of the
 // following stage (PV on half NKB of V stage NSV).
-template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB, bool PROJ = false>
+template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB, bool CAP, bool PROJ = false>
 __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
                                        const int (&vro)[DV / 32], const int (&xbl)[HPW],
                                        const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][DV / 32],
                                        f32x16 (&sout)[HPW], const bf16x8 (&pin)[HPW][2],
                                        const f32x16 (&ssm)[HPW], float den_a, float (&rowsum)[HPW],
-                                       bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4],
+                                       float (&mref)[HPW], bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4],
                                        const ProjIn<HPW>* proj = nullptr) {
   constexpr int NPV = DV / 32;
   constexpr int NSLOT = 8 + 2 * NPV;
+  constexpr int NOPS = CAP ? kSmOps : kSmOpsU;
   SmState sm[HPW];
+  // without the cap: the half's maximum first; the row sums take the
+  // factor now, the value accumulators after this stage's PV products
+  // (which still add weights taken against the old reference)
+  bool moved[HPW];
+  float fac[HPW];
+  if constexpr (!CAP) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      moved[hh] = update_ref(ssm[hh], mref[hh], fac[hh]);
+      rowsum[hh] *= fac[hh];
+    }
+  }
   ProjState pst[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) pst[hh] = ProjState{0.f, 0.f, 0.f};
@@ -931,17 +998,30 @@ __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
         mfma(O[hh][slot_db<NPV>(j)], ring[j & 3], pin[hh][slot_half<NPV>(j)]);
       }
 #pragma unroll
-      for (int u = 0; u < sm_count<NSLOT>(j); ++u)
-        sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh],
-              ssm[hh], den_a, rowsum[hh]);
+      for (int u = 0; u < sm_count<NSLOT, NOPS>(j); ++u) {
+        if constexpr (CAP)
+          sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh],
+                ssm[hh], den_a, rowsum[hh]);
+        else
+          sm_op_u(kSmU.op[sm_begin<NSLOT, NOPS>(j) + u].pass, kSmU.op[sm_begin<NSLOT, NOPS>(j) + u].idx,
+                  sm[hh], ssm[hh], mref[hh], rowsum[hh]);
+      }
       if constexpr (PROJ) proj_op<HPW>(j, *proj, pst[hh], hh);
     }
     // inside the slot: the MFMA first, then the LDS reads, then the VALU work
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    valu_group_n((sm_count<NSLOT>(j) + (PROJ && j <= 12 ? 1 : 0)) * HPW);
+    valu_group_n((sm_count<NSLOT, NOPS>(j) + (PROJ && j <= 12 ? 1 : 0)) * HPW);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (!CAP) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+      if (moved[hh]) {
+#pragma unroll
+        for (int db = 0; db < NPV; ++db) O[hh][db] *= fac[hh];
+      }
   }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
@@ -1140,14 +1220,15 @@ __device__ __forceinline__ void pair_store(char* smem, const bf16x8 (&a)[2], con
 }
 
 // One pipelined iteration for tile t in stage C.
-template <int HPW, int DV, bool TAIL, bool FUSED, int C>
+template <int HPW, int DV, bool TAIL, bool FUSED, bool CAP, int C>
 __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUSED>& c, int t, int last,
                                           const int (&kro)[8], const int (&vro)[DV / 32],
                                           const int (&xbl)[HPW], const bf16x8 (&qf)[HPW][8],
                                           f32x16 (&O)[HPW][DV / 32], f32x16 (&S0)[HPW],
                                           f32x16 (&S1)[HPW], bf16x8 (&P0)[HPW][2],
                                           bf16x8 (&P1)[HPW][2],
-                                          float den_a, float (&rowsum)[HPW], bf16x8 (&ring)[4]) {
+                                          float den_a, float (&rowsum)[HPW], float (&mref)[HPW],
+                                          bf16x8 (&ring)[4]) {
   constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
   // K and V of tile t+2 into the stage that held tile t-1, and the cells of
   // tile t+3 into the slot that held tile t's (expanded two iterations ago);
@@ -1162,7 +1243,7 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUS
   if constexpr (FUSED && DV == 128) pair_load<DV, NN>(smem, pv);
   if constexpr (!FUSED) bias_cells_load<HPW, DV, NN>(smem, c.wave, bc);
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
-  fstage<HPW, DV, C, NXT, 0, C, 1>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, P1, ring);
+  fstage<HPW, DV, C, NXT, 0, C, 1, CAP>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, mref, P1, ring);
   if constexpr (FUSED && DV != 128) pair_load<DV, NN>(smem, pv);
   // the exponent offsets of tile t+2, read by the next iteration
   if constexpr (FUSED && DV != 128) pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
@@ -1179,9 +1260,10 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUS
     for (int hh = 0; hh < HPW; ++hh)
       pj.dst[hh] = reinterpret_cast<float*>(smem + FP<DV>::XB0 + NN * FP<DV>::XBS) +
                    (c.wave * HPW + hh) * 64 + entry;
-    fstage<HPW, DV, C, NXT, 1, NXT, 0, true>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, P0, ring, &pj);
+    fstage<HPW, DV, C, NXT, 1, NXT, 0, CAP, true>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, mref, P0,
+                                                  ring, &pj);
   } else {
-    fstage<HPW, DV, C, NXT, 1, NXT, 0>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, P0, ring);
+    fstage<HPW, DV, C, NXT, 1, NXT, 0, CAP>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, mref, P0, ring);
   }
   tile_barrier();
 }
@@ -1216,12 +1298,51 @@ __device__ __forceinline__ void softmax_exp(const f32x16& t, float den_a, float&
   }
 }
 
+// The weights without the cap, 2^(u - reference) for 16 base-2 exponents u,
+// after moving the reference (update_ref) and rescaling what O and the row
+// sum hold; packed and summed as softmax_exp.  MASK as there.
+template <bool MASK, int NPV>
+__device__ __forceinline__ void softmax_exp_u(const f32x16& u, float& mref, float& rowsum,
+                                              f32x16 (&O)[NPV], bf16x8 (&p)[2], int lim) {
+  float f;
+  if (update_ref(u, mref, f)) {
+#pragma unroll
+    for (int db = 0; db < NPV; ++db) O[db] *= f;
+  }
+  rowsum *= f;
+  float w[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) w[x] = __builtin_amdgcn_exp2f(u[x] - mref);
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    bf16x2 pr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x2 two = {w[8 * half + 2 * m], w[8 * half + 2 * m + 1]};
+      pr[m] = __builtin_convertvector(two, bf16x2);
+      if constexpr (MASK) pr[m] = mask_pair(pr[m], 16 * half + 2 * m, lim);
+      rowsum = __builtin_amdgcn_fdot2_f32_bf16(pr[m], ones, rowsum, false);
+    }
+    bf16x8 f8;
+    __builtin_memcpy(&f8, pr, 16);
+    p[half] = f8;
+  }
+}
+// The weights of one half, with or without the cap.
+template <bool CAP, bool MASK, int NPV>
+__device__ __forceinline__ void softmax_any(const f32x16& t, float den_a, float& rowsum, float& mref,
+                                            f32x16 (&O)[NPV], bf16x8 (&p)[2], int lim) {
+  if constexpr (CAP) softmax_exp<MASK>(t, den_a, rowsum, p, lim);
+  else softmax_exp_u<MASK, NPV>(t, mref, rowsum, O, p, lim);
+}
+
 // Last tile (stage C): PV of both halves and the softmax of its second half.
-template <int HPW, int DV, bool TAIL, int C>
+template <int HPW, int DV, bool TAIL, bool CAP, int C>
 __device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, const int (&vro)[DV / 32],
                                           f32x16 (&O)[HPW][DV / 32], const f32x16 (&S1)[HPW],
                                           const bf16x8 (&P0)[HPW][2], float den_a,
-                                          float (&rowsum)[HPW]) {
+                                          float (&rowsum)[HPW], float (&mref)[HPW]) {
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -1233,7 +1354,8 @@ __device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, cons
   bf16x8 P1[HPW][2];
   const int lim = klim_half1 - 8 * lane_g();
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) softmax_exp<TAIL>(S1[hh], den_a, rowsum[hh], P1[hh], lim);
+  for (int hh = 0; hh < HPW; ++hh)
+    softmax_any<CAP, TAIL, DV / 32>(S1[hh], den_a, rowsum[hh], mref[hh], O[hh], P1[hh], lim);
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -1273,11 +1395,11 @@ __device__ __forceinline__ void k_read_offsets(int r, int g, int (&kro)[8]) {
 // offsets are loaded again here rather than kept from the start: holding
 // them past the pipelined loop costs more registers than that loop leaves.
 // The tile's exponent offsets were expanded two iterations before.
-template <int HPW, int DV, int C>
+template <int HPW, int DV, bool CAP, int C>
 __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpos0, int Sq, const char* smem,
                                              const int (&vro)[DV / 32], const int (&xbl)[HPW],
                                              f32x16 (&O)[HPW][DV / 32], float alpha, float den_a,
-                                             float (&rowsum)[HPW]) {
+                                             float (&rowsum)[HPW], float (&mref)[HPW]) {
   // opaque to the compiler, so that it reloads instead of reusing the values
   // read before the loop
   int lane = (int)threadIdx.x & 63;
@@ -1309,7 +1431,8 @@ __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpo
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 P[HPW][2];
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) softmax_exp<true>(sc[kb][hh], den_a, rowsum[hh], P[hh], lim - 32 * kb);
+    for (int hh = 0; hh < HPW; ++hh)
+      softmax_any<CAP, true, DV / 32>(sc[kb][hh], den_a, rowsum[hh], mref[hh], O[hh], P[hh], lim - 32 * kb);
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -1328,15 +1451,17 @@ __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpo
 // ends the sequence is copied with its rows past the end clamped to its last
 // row and those keys masked (p = 0); query rows past Sq read row Sq - 1 and
 // store nothing.
-template <int HPW, int DV, bool SPLIT, bool TAIL, bool FUSED>
-__global__ __launch_bounds__(64 * (kHeads / HPW), 1)
-void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                       const __bf16* __restrict__ v, const float* __restrict__ bias,
-                                       const __bf16* __restrict__ pair, const __bf16* __restrict__ wt,
-                                       __bf16* __restrict__ out, float* __restrict__ ws, int Sq,
-                                       int S, int q_offset, int tiles_per_split,
-                                       int64_t bias_batch_stride, int bias_group, float alpha,
-                                       float beta_mul, float den_a) {
+// CAP: the soft cap with its fixed maximum; otherwise the online softmax
+// with a running reference maximum per row (bias, value width 128).
+template <int HPW, int DV, bool SPLIT, bool TAIL, bool FUSED, bool CAP>
+__device__ __forceinline__ void fast_attention(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                               const __bf16* __restrict__ v, const float* __restrict__ bias,
+                                               const __bf16* __restrict__ pair, const __bf16* __restrict__ wt,
+                                               __bf16* __restrict__ out, float* __restrict__ ws, int Sq,
+                                               int S, int q_offset, int tiles_per_split,
+                                               int64_t bias_batch_stride, int bias_group, float alpha,
+                                               float beta_mul, float den_a) {
+  static_assert(CAP || (DV == 128 && !FUSED), "without the cap: value width 128, compact bias");
   using L = FP<DV>;
   using Ctx = FastCtx<HPW, DV, FUSED>;
   constexpr int NT = 64 * (kHeads / HPW);
@@ -1425,9 +1550,11 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
 
   f32x16 O[HPW][NPV];
   float rowsum[HPW];
+  float mref[HPW];  // reference maximum of the row without the cap (base 2)
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     rowsum[hh] = 0.f;
+    mref[hh] = -1e30f;
 #pragma unroll
     for (int db = 0; db < NPV; ++db) O[hh][db] = f32x16{};
   }
@@ -1462,7 +1589,7 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
       mfma(S0[hh], kfrag<DV, 0>(smem, kro, 0, kc), qf[hh][kc]);
       mfma(S1[hh], kfrag<DV, 0>(smem, kro, 1, kc), qf[hh][kc]);
     }
-    softmax_exp<TAIL>(S0[hh], den_a, rowsum[hh], P0[hh], klim - 8 * g);
+    softmax_any<CAP, TAIL, NPV>(S0[hh], den_a, rowsum[hh], mref[hh], O[hh], P0[hh], klim - 8 * g);
   }
   // iteration 0 copies tile 3's cells into slot 0, which other waves may
   // still be reading for tile 0 above (later slots are two barriers past
@@ -1481,33 +1608,41 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
   int t = 0;
   while (true) {
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, FUSED, 0>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, CAP, 0>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum,
+                                            mref, ring);
     ++t;
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, FUSED, 1>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, CAP, 1>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum,
+                                            mref, ring);
     ++t;
     if (t >= lastp) break;
-    fast_iter<HPW, DV, TAIL, FUSED, 2>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum, ring);
+    fast_iter<HPW, DV, TAIL, FUSED, CAP, 2>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum,
+                                            mref, ring);
     ++t;
   }
   switch (lastp % 3) {
-    case 0: fast_tail<HPW, DV, TAIL, 0>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum); break;
-    case 1: fast_tail<HPW, DV, TAIL, 1>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum); break;
-    default: fast_tail<HPW, DV, TAIL, 2>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum); break;
+    case 0: fast_tail<HPW, DV, TAIL, CAP, 0>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref); break;
+    case 1: fast_tail<HPW, DV, TAIL, CAP, 1>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref); break;
+    default: fast_tail<HPW, DV, TAIL, CAP, 2>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref); break;
   }
   if constexpr (TAIL) {
     if (c.tile_end > 0) {  // uniform; the tile was loaded and its offsets expanded before
       switch (last % 3) {
-        case 0: fast_partial<HPW, DV, 0>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum); break;
-        case 1: fast_partial<HPW, DV, 1>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum); break;
-        default: fast_partial<HPW, DV, 2>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum); break;
+        case 0: fast_partial<HPW, DV, CAP, 0>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
+                                           mref); break;
+        case 1: fast_partial<HPW, DV, CAP, 1>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
+                                           mref); break;
+        default: fast_partial<HPW, DV, CAP, 2>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
+                                           mref); break;
       }
     }
   }
   if constexpr (SPLIT) {
     // partial numerator rows [split][b][pos][h][DV] and denominators
     // [split][b][pos][h], float32; lane (r, g) holds channels
-    // 32 db + 8 j + 4 g .. + 3 of its row (32 x 32 accumulator layout)
+    // 32 db + 8 j + 4 g .. + 3 of its row (32 x 32 accumulator layout).
+    // Without the cap the rows are normalised and the denominator slot
+    // holds reference + log2(row sum) instead.
     const int64_t rows = (int64_t)gridDim.y * Sq * kHeads;
     float* wn = ws + ((int64_t)split * gridDim.y + b) * Sq * kHeads * DV;
     float* wd = ws + (int64_t)gridDim.z * rows * DV + ((int64_t)split * gridDim.y + b) * Sq * kHeads;
@@ -1515,6 +1650,7 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = w * HPW + hh;
       const float tot = rowsum[hh] + __shfl_xor(rowsum[hh], 32);
+      const float inv = CAP ? 1.f : 1.f / tot;
       float* nrow = wn + ((int64_t)(qpos0 + r) * kHeads + h) * DV + 4 * g;
       if (TAIL && qpos0 + r >= Sq) continue;
 #pragma unroll
@@ -1522,9 +1658,9 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4 x = {O[hh][db][4 * j], O[hh][db][4 * j + 1], O[hh][db][4 * j + 2], O[hh][db][4 * j + 3]};
-          *reinterpret_cast<f32x4*>(nrow + 32 * db + 8 * j) = x;
+          *reinterpret_cast<f32x4*>(nrow + 32 * db + 8 * j) = CAP ? x : x * inv;
         }
-      if (g == 0) wd[(int64_t)(qpos0 + r) * kHeads + h] = tot;
+      if (g == 0) wd[(int64_t)(qpos0 + r) * kHeads + h] = CAP ? tot : mref[hh] + __builtin_amdgcn_logf(tot);
     }
   } else {
     __syncthreads();  // the output staging reuses the tile buffers
@@ -1534,6 +1670,33 @@ void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf1
     copy_output<__bf16, NT, DV>(smem, out + ((int64_t)b * Sq + qpos0) * kHeads * DV, tid,
                                 TAIL ? min(kBlockPos, Sq - qpos0) : kBlockPos);
   }
+}
+
+template <int HPW, int DV, bool SPLIT, bool TAIL, bool FUSED>
+__global__ __launch_bounds__(64 * (kHeads / HPW), 1)
+void biased_mqa_fwd_bf16_capped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                       const __bf16* __restrict__ v, const float* __restrict__ bias,
+                                       const __bf16* __restrict__ pair, const __bf16* __restrict__ wt,
+                                       __bf16* __restrict__ out, float* __restrict__ ws, int Sq,
+                                       int S, int q_offset, int tiles_per_split,
+                                       int64_t bias_batch_stride, int bias_group, float alpha,
+                                       float beta_mul, float den_a) {
+  fast_attention<HPW, DV, SPLIT, TAIL, FUSED, true>(q, k, v, bias, pair, wt, out, ws, Sq, S, q_offset,
+                                                    tiles_per_split, bias_batch_stride, bias_group,
+                                                    alpha, beta_mul, den_a);
+}
+template <int HPW, bool SPLIT, bool TAIL>
+__global__ __launch_bounds__(64 * (kHeads / HPW), 1)
+void biased_mqa_fwd_bf16_uncapped_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                         const __bf16* __restrict__ v, const float* __restrict__ bias,
+                                         const __bf16* __restrict__ pair, const __bf16* __restrict__ wt,
+                                         __bf16* __restrict__ out, float* __restrict__ ws, int Sq,
+                                         int S, int q_offset, int tiles_per_split,
+                                         int64_t bias_batch_stride, int bias_group, float alpha,
+                                         float beta_mul, float den_a) {
+  fast_attention<HPW, 128, SPLIT, TAIL, false, false>(q, k, v, bias, pair, wt, out, ws, Sq, S, q_offset,
+                                                      tiles_per_split, bias_batch_stride, bias_group,
+                                                      alpha, beta_mul, den_a);
 }
 
 // Merge of the key ranges' partial states into the output (one thread per 4
@@ -1583,7 +1746,7 @@ void merge_partials_kernel(const float* __restrict__ ws, T* __restrict__ out, in
   }
 }
 
-template <int DV, bool TAIL, bool FUSED>
+template <int DV, bool TAIL, bool FUSED, bool CAP>
 hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
                          float den_a) {
   constexpr int HPW = kFastHeadsPerWave;
@@ -1596,14 +1759,18 @@ hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, f
   __bf16* out = static_cast<__bf16*>(a.out);
   const __bf16* pair = static_cast<const __bf16*>(a.pair);
   const __bf16* wt = static_cast<const __bf16*>(a.weight);
+  constexpr auto kern1 = CAP ? biased_mqa_fwd_bf16_capped_kernel<HPW, DV, false, TAIL, FUSED>
+                             : biased_mqa_fwd_bf16_uncapped_kernel<HPW, false, TAIL>;
+  constexpr auto kernz = CAP ? biased_mqa_fwd_bf16_capped_kernel<HPW, DV, true, TAIL, FUSED>
+                             : biased_mqa_fwd_bf16_uncapped_kernel<HPW, true, TAIL>;
   if (splits == 1) {
-    hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, false, TAIL, FUSED>), grid,
+    hipLaunchKernelGGL(kern1, grid,
                        dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, pair, wt, out, nullptr,
                        (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
                        (int)a.bias_group, alpha, beta_mul, den_a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((biased_mqa_fwd_bf16_capped_kernel<HPW, DV, true, TAIL, FUSED>), grid,
+  hipLaunchKernelGGL(kernz, grid,
                      dim3(64 * (kHeads / HPW)), 0, stream, q, k, v, a.bias, pair, wt, out, a.ws,
                      (int)a.Sq, (int)a.Sk, (int)a.q_offset, tiles, a.bias_batch_stride,
                      (int)a.bias_group, alpha, beta_mul, den_a);
@@ -1611,20 +1778,22 @@ hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, f
   if (e != hipSuccess) return e;
   const int64_t rows = a.B * a.Sq * kHeads;
   const int64_t threads = rows * (DV / 4);
-  hipLaunchKernelGGL((merge_partials_kernel<DV, __bf16, false>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((merge_partials_kernel<DV, __bf16, !CAP>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, a.ws, out, rows, splits);
   return hipGetLastError();
 }
 
-template <int DV>
+template <int DV, bool CAP>
 hipError_t launch_fast(const AttnLaunch& a, hipStream_t stream, float alpha, float beta_mul,
                        float den_a) {
   const bool tail = a.Sk % kTileKeys != 0 || a.Sq % kBlockPos != 0;
-  if (a.pair)  // bias projected in the kernel from the pair representation
-    return tail ? launch_fast_t<DV, true, true>(a, stream, alpha, beta_mul, den_a)
-                : launch_fast_t<DV, false, true>(a, stream, alpha, beta_mul, den_a);
-  return tail ? launch_fast_t<DV, true, false>(a, stream, alpha, beta_mul, den_a)
-              : launch_fast_t<DV, false, false>(a, stream, alpha, beta_mul, den_a);
+  if constexpr (CAP) {
+    if (a.pair)  // bias projected in the kernel from the pair representation
+      return tail ? launch_fast_t<DV, true, true, true>(a, stream, alpha, beta_mul, den_a)
+                  : launch_fast_t<DV, false, true, true>(a, stream, alpha, beta_mul, den_a);
+  }
+  return tail ? launch_fast_t<DV, true, false, CAP>(a, stream, alpha, beta_mul, den_a)
+              : launch_fast_t<DV, false, false, CAP>(a, stream, alpha, beta_mul, den_a);
 }
 
 template <typename T, bool CAPPED>
@@ -1641,8 +1810,12 @@ hipError_t launch_typed(const AttnLaunch& a, hipStream_t stream) {
     den_a = 0.f;
   }
   if constexpr (CAPPED && sizeof(T) == 2) {
-    return a.Dv == 192 ? launch_fast<192>(a, stream, alpha, beta_mul, den_a)
-                       : launch_fast<128>(a, stream, alpha, beta_mul, den_a);
+    return a.Dv == 192 ? launch_fast<192, true>(a, stream, alpha, beta_mul, den_a)
+                       : launch_fast<128, true>(a, stream, alpha, beta_mul, den_a);
+  } else if constexpr (sizeof(T) == 2) {
+    // bf16 without the cap (value width 128, compact bias: the only form the
+    // boundary accepts): the same kernel with the online softmax
+    return launch_fast<128, false>(a, stream, alpha, beta_mul, den_a);
   } else {
     const bool tail = a.Sk % kTileKeys != 0 || a.Sq % kBlockPos != 0;
     const int splits = (int)a.kv_splits;

@@ -323,9 +323,10 @@ def test_attention_tails(case):
     print(f"  tails {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
 
 
-# The generic kernel (float32 inputs, or no cap) off the tile grid: the same
-# clamped staging and masking, with the online recurrence when uncapped (a
-# masked key must take no part in the running maximum either).
+# Float32 inputs, or no cap, off the tile grid (the float32 cases on the
+# generic kernel, the bf16 ones on the uncapped form of the bf16 kernel): the
+# same clamped staging and masking, with the online recurrence when uncapped
+# (a masked key must take no part in the running maximum either).
 GENERIC_TAILS = [
     # dtype, cap, B, S, q_rows (start, stop) or None
     ("f32", 5.0, 1, 1, None),           # one key, one query
@@ -375,7 +376,7 @@ def test_generic_kernel_tails(case):
     print(f"  generic tails {case}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}", flush=True)
 
 
-# Key ranges on the generic kernel: with the cap the ranges share the fixed
+# Key ranges on the float32 kernel and the uncapped bf16 kernel: with the cap the ranges share the fixed
 # maximum and their sums add; without it each range keeps its own running
 # maximum and the merge takes the page's update equations across ranges
 # (with bias std 60 the ranges' maxima differ by tens).
@@ -680,6 +681,31 @@ def test_saturated_logits(route, dt, cap):
     assert float(np.abs(bias64).max()) > 20 * max(cap, 1.0)
     ref = oracle.attention(L.q, L.k, L.v, bias64, scale=L.scale, cap=cap)
     ok, ma, rel = attention_ok(got, ref, dt)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
+@pytest.mark.parametrize("slope,splits", [(0.7, 1), (-0.7, 1), (0.7, 4), (3.0, 2)])
+def test_running_maximum_moves(slope, splits):
+    """Without the cap (bf16): a bias that rises along the keys by `slope`
+    per key cell moves the kernel's reference maximum every few tiles (a
+    steep rise, every tile); falling, the first tile's reference holds and
+    the later weights shrink toward 0.  Also with key ranges (each range its
+    own maxima, merged by log-sum-exp) on a query block.  2000 positions: a
+    partial last tile."""
+    S = 2000
+    L = workloads.make_custom(B=1, S=S, dtype="bf16", C=16, seed=77)
+    P = (S + 15) // 16
+    ramp = slope * np.arange(P, dtype=np.float64)
+    bias = np.ascontiguousarray(np.broadcast_to(ramp[None, None, :], (8, P, P)), dtype=np.float32)
+    t = upload(L)
+    rows = slice(0, S) if splits == 1 else slice(512, 1536)
+    q = t["q"][:, rows].contiguous()
+    out = biased_mqa_fwd(q, t["k"], t["v"], to_gpu(bias), scale=L.scale, softcap=0.0,
+                         q_offset=rows.start, kv_splits=splits)
+    got = to_host(out)
+    ref = oracle.attention_rows(L.q, L.k, L.v, bias[None].astype(np.float64),
+                                np.arange(rows.start, rows.stop), scale=L.scale, cap=0.0, batch=0)
+    ok, ma, rel = attention_ok(got[0], ref, "bf16")
     assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 

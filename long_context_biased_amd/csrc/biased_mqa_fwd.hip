@@ -1300,10 +1300,19 @@ __device__ __forceinline__ void softmax_exp(const f32x16& t, float den_a, float&
 
 // The weights without the cap, 2^(u - reference) for 16 base-2 exponents u,
 // after moving the reference (update_ref) and rescaling what O and the row
-// sum hold; packed and summed as softmax_exp.  MASK as there.
+// sum hold; packed and summed as softmax_exp.  MASK as there; a masked key
+// takes exponent -inf before the maximum is formed, so that the finite but
+// meaningless score of a clamped padding row can neither move the reference
+// nor take weight (the maximum runs over keys that exist).
 template <bool MASK, int NPV>
-__device__ __forceinline__ void softmax_exp_u(const f32x16& u, float& mref, float& rowsum,
+__device__ __forceinline__ void softmax_exp_u(const f32x16& u_in, float& mref, float& rowsum,
                                               f32x16 (&O)[NPV], bf16x8 (&p)[2], int lim) {
+  f32x16 u = u_in;
+  if constexpr (MASK) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x)
+      if (16 * (x >> 3) + (x & 7) >= lim) u[x] = -__builtin_inff();
+  }
   float f;
   if (update_ref(u, mref, f)) {
 #pragma unroll

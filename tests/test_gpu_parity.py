@@ -169,9 +169,13 @@ def test_attention_variant_sampled(hot):
     _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=7))
 
 
-@pytest.mark.parametrize("name", ["stress", "stress_f32"])
-def test_attention_stress_sampled(name):
-    L = workloads.make_layer(name)
+@pytest.mark.parametrize("name,hot", [("stress", False), ("stress", True), ("stress_f32", False)],
+                         ids=["bf16_base", "bf16_hot", "f32_base"])
+def test_attention_stress_sampled(name, hot):
+    """S = 16384.  At the workload's own distribution the bf16 outputs are
+    about 1e-2, so the hot companion (q, k, v ~ N(0,1), bias x 2) is what
+    rejects a kernel that drops a term of the logit at this length."""
+    L = workloads.make_layer(name, hot=hot)
     _, out = _run_layer(L, "cuda")
     _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=3, extra=8))
 
@@ -409,6 +413,45 @@ def test_generic_kernel_key_ranges(case):
         assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
+# bf16 without the cap, a last tile that ends early: the padding rows of the
+# tile are copies of the last real key's final 16 bytes, so their scores are
+# finite and unrelated to any real logit.  With q = 4 in every dimension and
+# the last key 4 on dimensions 120..127 (0 elsewhere) a padding score is 16x
+# the last key's (about 261 against 16 in base-2 units); were it allowed into
+# the running maximum, every real weight would underflow and the output would
+# be 0/0.  The maximum must run over keys that exist (page "Making Full-Context
+# AlphaGenome Fit on an RTX 3090", section "Online softmax, one block at a
+# time").  Plain call (single tile, partial last tile) and key ranges.
+PADDING_MAX = [
+    # S, kv_splits
+    (48, 1),     # one tile: prologue and last-tile mask
+    (100, 1),    # a partial last tile taken on its own
+    (100, 2),    # two one-tile ranges, the second partial
+    (1000, 4),   # ranges of 4 tiles, the last partial
+]
+
+
+@pytest.mark.parametrize("case", PADDING_MAX, ids=lambda c: "S%d_z%d" % c)
+def test_uncapped_padding_keys_do_not_move_the_maximum(case):
+    S, z = case
+    L = workloads.make_custom(B=1, S=S, dtype="bf16", C=16, seed=2100 + S, qkv_std=1.0 / math.sqrt(128.0),
+                              bias_std=2.0)
+    L.cap = 0.0
+    q = np.full(L.q.shape, 4.0, np.float32)
+    k = np.asarray(oracle.as_f64(L.k), np.float32).copy()
+    k[:, S - 1] = 0.0
+    k[:, S - 1, :, 120:128] = 4.0
+    L.q = workloads.f32_to_bf16_bits(q)
+    L.k = workloads.f32_to_bf16_bits(k)
+    out = _run_ex(L, range(0, S), kv_splits=z)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    ref = oracle.attention_rows(L.q, L.k, L.v, _oracle_bias(L), np.arange(S), scale=L.scale,
+                                cap=0.0, batch=0)
+    ok, ma, rel = attention_ok(out[0], ref, "bf16")
+    print(f"  padding max S={S} z={z}: max-abs {ma:.3g} rel-L2 {rel:.3g}", flush=True)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_attention_long_sampled():
     """S = 65536 (4096 compact cells per side, 1024 key tiles, a 512 MiB
     bias), far past the workloads' lengths: sampled rows, through the
@@ -570,15 +613,38 @@ def test_pair_form(case):
           flush=True)
 
 
-@pytest.mark.parametrize("name,hot", [("full", False), ("full", True), ("variant", False)],
-                         ids=["full_base", "full_hot", "variant"])
+@pytest.mark.parametrize("name,hot", [("full", False), ("full", True), ("variant", False),
+                                      ("variant", True), ("stress", False), ("stress", True)],
+                         ids=["full_base", "full_hot", "variant_base", "variant_hot", "stress_base",
+                              "stress_hot"])
 def test_pair_form_full_sampled(name, hot):
-    """The full-context and variant workloads through the pair form, sampled
-    rows (every item of the variant, whose ref/alt items share a pair)."""
-    L = workloads.make_layer(name, layer=2, hot=hot)
+    """The full-context, variant and stress workloads through the pair form,
+    sampled rows (every item of the variant, whose ref/alt items share a
+    pair)."""
+    L = workloads.make_layer(name, layer=2 if name == "full" else 0, hot=hot)
     out, two = _run_pair(L, range(0, L.S), 1)
     _check_rows(L, out, _oracle_bias(L), sample_rows(L.S, seed=21))
     assert float(np.max(np.abs(out - two))) <= 2e-2
+
+
+@pytest.mark.parametrize("hot", [False, True], ids=["base", "hot"])
+def test_pair_form_full_layer_every_output(hot):
+    """Every output (8192 positions x 8 heads x 128) of a full-context layer
+    through the pair form, the call the benchmark times, against the dense
+    oracle."""
+    import time
+    L = workloads.make_layer("full", layer=4, hot=hot)
+    t = upload(L)
+    out = pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], scale=L.scale,
+                              softcap=L.cap)
+    torch.cuda.synchronize()
+    got = to_host(out)
+    t0 = time.time()
+    ref = oracle.attention(L.q, L.k, L.v, _oracle_bias(L), scale=L.scale, cap=L.cap)
+    ok, ma, rel = attention_ok(got, ref, "bf16")
+    print(f"  full layer, every output{' (hot)' if hot else ''}: max-abs {ma:.3g} rel-L2 {rel:.3g} "
+          f"(oracle {time.time() - t0:.1f} s)", flush=True)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
 @pytest.mark.parametrize("dt,cap", [("f32", 5.0), ("bf16", 0.0)])

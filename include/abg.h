@@ -52,8 +52,9 @@ typedef enum abg_status {
   ABG_ERR_UNSUPPORTED = 3, /* valid request that this library does not implement */
   ABG_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
   ABG_ERR_VALUE = 5,       /* a scalar argument is not finite or out of range    */
-  ABG_ERR_ALIAS = 6,       /* the output overlaps an input                       */
-  ABG_ERR_DEVICE = 7       /* the HIP runtime reported an error                  */
+  ABG_ERR_DEVICE = 6,      /* the HIP runtime reported an error                  */
+  ABG_ERR_ALIAS = 7        /* the output overlaps an input (appended after the   */
+                           /* first six codes, which keep their values)          */
 } abg_status;
 
 typedef enum abg_dtype {

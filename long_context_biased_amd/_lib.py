@@ -20,7 +20,7 @@ ABG_F32 = 0
 ABG_BF16 = 1
 
 STATUS = {0: "ABG_OK", 1: "ABG_ERR_NULL", 2: "ABG_ERR_SHAPE", 3: "ABG_ERR_UNSUPPORTED",
-          4: "ABG_ERR_ALIGN", 5: "ABG_ERR_VALUE", 6: "ABG_ERR_ALIAS", 7: "ABG_ERR_DEVICE"}
+          4: "ABG_ERR_ALIGN", 5: "ABG_ERR_VALUE", 6: "ABG_ERR_DEVICE", 7: "ABG_ERR_ALIAS"}
 
 #: Every symbol include/abg.h declares.
 EXPORTS = ("abg_abi_version", "abg_status_string", "abg_last_error",

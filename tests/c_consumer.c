@@ -30,6 +30,13 @@ int main(void) {
 
   expect(abg_abi_version() == ABG_ABI_VERSION, "abi version");
   expect(strcmp(abg_status_string(ABG_OK), "ABG_OK") == 0, "status name");
+  /* The status codes are part of the ABI: the first seven keep the values
+   * of the library's first contract, ABG_ERR_ALIAS was appended after them. */
+  expect(ABG_ERR_NULL == 1 && ABG_ERR_SHAPE == 2 && ABG_ERR_UNSUPPORTED == 3 &&
+             ABG_ERR_ALIGN == 4 && ABG_ERR_VALUE == 5 && ABG_ERR_DEVICE == 6 &&
+             ABG_ERR_ALIAS == 7,
+         "status code values");
+  expect(strcmp(abg_status_string(6), "ABG_ERR_DEVICE") == 0, "code 6 is ABG_ERR_DEVICE");
 
   /* Eight query heads are required. */
   st = abg_biased_mqa_fwd(q, k, v, bias, out, 1, 8192, 4, 128, 128, 0, 1,

@@ -15,7 +15,7 @@ from long_context_biased_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "abg.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, VALUE, ALIAS, DEVICE = range(8)
+OK, NULL, SHAPE, UNSUP, ALIGN, VALUE, DEVICE, ALIAS = range(8)
 
 # Fake, distinct, 16-byte aligned "device" addresses: validation never
 # dereferences them, and every call below fails validation.

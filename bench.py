@@ -96,7 +96,9 @@ def load_counters(path):
             return None
         return {"hbm_bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
                 "mfma_flops_per_launch": float(kv["mfma_flops_per_launch"]),
-                "mfma_busy_frac": float(kv["mfma_busy_frac"])}
+                "mfma_busy_frac": float(kv["mfma_busy_frac"]),
+                "cycles_per_launch": float(kv["cycles_per_launch"]) if "cycles_per_launch" in kv
+                else None}
     except (OSError, KeyError, ValueError):
         return None
 
@@ -118,16 +120,37 @@ def environment(torch, dev):
     return env
 
 
+def host_cpu():
+    """This host's CPU model, the cores this process may run on and the
+    logical CPUs of the machine."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "cores": affinity, "logical_cpus": os.cpu_count()}
+
+
 def cpu_baseline(host_layers):
     """The oracle (unchanged) on a bounded sample of the workload: the first
     layers (projection + all 8192 x 8 output rows each), timed on this host's
-    cores."""
+    cores.  numpy's elementwise steps run on one thread and its matrix
+    products on the BLAS pool; ``cores`` is what the process may use, and
+    ``blas_threads`` the pool's size."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = None
     t0 = time.perf_counter()
     for layer in host_layers:
         bias = oracle.project_pair_bias(layer.pair, layer.weight)
@@ -135,10 +158,83 @@ def cpu_baseline(host_layers):
     dt = time.perf_counter() - t0
     L0 = host_layers[0]
     fl = attn_flops(L0.B, L0.S, Dv=L0.v.shape[-1]) * len(host_layers)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    hc = host_cpu()
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": hc["cores"],
+            "kind": "oracle", "cpu_model": hc["cpu_model"], "logical_cpus": hc["logical_cpus"],
+            "blas_threads": blas, "wall_s": round(dt, 2),
             "sample": (f"{len(host_layers)} of the 9 layers (projection + all {L0.S} positions x "
-                       f"8 heads each), float64 numpy, {dt:.1f} s wall; BLAS threads = cores")}
+                       f"8 heads each), float64 numpy, {dt:.1f} s wall; elementwise steps on one "
+                       f"thread, matrix products on {blas} BLAS threads")}
+
+
+class ClockSampler:
+    """Reads the GPU's shader clock and power from sysfs (hwmon of the amdgpu
+    device) every few milliseconds while a timed region runs, in a host
+    thread that makes no GPU call.  Figures are None where the files are not
+    readable."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        self.period = period_s
+        self.freq, self.power = [], []
+        self.cap_w = None
+        self.files = {}
+        for hw in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+            try:
+                with open(os.path.join(hw, "name")) as f:
+                    if f.read().strip() != "amdgpu":
+                        continue
+            except OSError:
+                continue
+            for key, name in (("freq", "freq1_input"), ("power", "power1_average"),
+                              ("power_in", "power1_input"), ("cap", "power1_cap")):
+                fn = os.path.join(hw, name)
+                if os.access(fn, os.R_OK):
+                    self.files.setdefault(key, fn)
+            if self.files:
+                break
+        if "cap" in self.files:
+            v = self._read("cap")
+            self.cap_w = v / 1e6 if v is not None else None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self, key):
+        fn = self.files.get(key)
+        if fn is None:
+            return None
+        try:
+            with open(fn) as f:
+                return float(f.read().strip())
+        except (OSError, ValueError):
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            fq = self._read("freq")
+            if fq is not None:
+                self.freq.append(fq / 1e6)
+            pw = self._read("power") if "power" in self.files else self._read("power_in")
+            if pw is not None:
+                self.power.append(pw / 1e6)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        def med(x):
+            return round(float(np.median(x)), 1) if x else None
+        return {"sclk_mhz_median": med(self.freq), "sclk_samples": len(self.freq),
+                "power_w_median": med(self.power), "power_cap_w": self.cap_w,
+                "source": "sysfs hwmon (amdgpu), sampled during the timed region"
+                          if self.files else "not readable on this host"}
 
 
 def attention_only(args, torch, dev, biased_mqa_fwd, workloads):
@@ -193,18 +289,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--layers", type=int, default=9)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers per step (default 9 for full, mid and shard; 1 for variant and "
+                         "stress, whose step is one call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=3,
                     help="layers in the oracle's timed sample (about 4-5 s each on 16 cores)")
     ap.add_argument("--dv", type=int, default=128, choices=(128, 192),
                     help="value width (192 is the released checkpoint's; the headline "
                          "workload uses 128)")
-    ap.add_argument("--workload", default="full", choices=("full", "mid", "shard"),
+    ap.add_argument("--workload", default="full",
+                    choices=("full", "mid", "shard", "variant", "stress"),
                     help="full: the full-context layers (the headline); mid: S=2048 layers; "
                          "shard: one GPU's share of a full-context layer under sequence "
                          "parallelism over 8 GPUs (1024 query positions at offset 3072, all "
-                         "8192 keys)")
+                         "8192 keys); variant: one call on 8 items of S=8192 (4 ref/alt pairs, "
+                         "one pair representation per pair); stress: one call at S=16384")
     ap.add_argument("--kv-splits", default=None,
                     help="key ranges per attention call (an integer or 'auto'; default: 1 for "
                          "full, auto otherwise)")
@@ -241,7 +341,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
-    n_layers = args.layers
+    wl = args.workload
+    n_layers = args.layers if args.layers is not None else (
+        1 if wl in ("variant", "stress") else 9)
     if args.attention_only:
         attention_only(args, torch, dev, biased_mqa_fwd, workloads)
         return
@@ -253,31 +355,35 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     from long_context_biased_amd import auto_kv_splits, workspace_bytes
-    wl = args.workload
     if wl != "full":
         args.no_cpu_baseline = True
     t0 = time.perf_counter()
     layers, host = [], []
     for li in range(n_layers):
-        L = workloads.make_layer("mid" if wl == "mid" else "full", layer=li, Dv=args.dv)
+        L = workloads.make_layer({"mid": "mid", "variant": "variant", "stress": "stress"}.get(
+            wl, "full"), layer=li, Dv=args.dv)
         if li < max(1, args.cpu_layers):
             host.append(L)
         t = {n: to_gpu(getattr(L, n)) for n in ("q", "k", "v", "pair", "weight")}
         P = -(-L.S // 16)
         q_off, Sq = (3072, 1024) if wl == "shard" else (0, L.S)
         t["q"] = t["q"][:, q_off:q_off + Sq].contiguous()
-        t["bias"] = torch.empty((8, P, P), dtype=torch.float32, device=dev)
-        t["out"] = torch.empty((1, Sq, 8, args.dv), dtype=t["q"].dtype, device=dev)
+        n_pairs = L.pair.shape[0]
+        t["group"] = L.bias_group
+        t["bias"] = torch.empty((n_pairs, 8, P, P), dtype=torch.float32, device=dev)
+        t["out"] = torch.empty((L.B, Sq, 8, args.dv), dtype=t["q"].dtype, device=dev)
         ks = args.kv_splits if args.kv_splits is not None else ("1" if wl == "full" else "auto")
-        z = auto_kv_splits(1, Sq, L.S) if ks == "auto" else int(ks)
+        z = auto_kv_splits(L.B, Sq, L.S) if ks == "auto" else int(ks)
         t["z"], t["q_off"], t["Sq"] = z, q_off, Sq
-        nws = workspace_bytes(1, Sq, 8, args.dv, z)
+        nws = workspace_bytes(L.B, Sq, 8, args.dv, z)
         t["ws"] = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev) if nws > 0 else None
         layers.append(t)
     torch.cuda.synchronize()
     log(f"inputs: {n_layers} layers generated and uploaded in {time.perf_counter() - t0:.1f} s")
     host0 = host[0]
     S = host0.S
+    Bw = host0.B
+    n_pairs = host0.pair.shape[0]
     P = -(-S // 16)
     scale = host0.scale
     cap = host0.cap
@@ -292,8 +398,8 @@ def main():
             if events is not None:
                 events[li][1].record(stream)
             biased_mqa_fwd(t["q"], t["k"], t["v"], t["bias"], out=t["out"], scale=scale,
-                           softcap=cap, q_offset=t["q_off"], kv_splits=t["z"],
-                           workspace=t["ws"])
+                           softcap=cap, bias_group=t["group"], q_offset=t["q_off"],
+                           kv_splits=t["z"], workspace=t["ws"])
             if events is not None:
                 events[li][2].record(stream)
 
@@ -302,31 +408,35 @@ def main():
             if events is not None:
                 events[li][0].record(stream)
             pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], out=t["out"],
-                                scale=scale, softcap=cap, q_offset=t["q_off"],
-                                kv_splits=t["z"], workspace=t["ws"])
+                                scale=scale, softcap=cap, pair_group=t["group"],
+                                q_offset=t["q_off"], kv_splits=t["z"], workspace=t["ws"])
             if events is not None:
                 events[li][1].record(stream)
                 events[li][2].record(stream)
+
+    clocks = {}
 
     def measure(step):
         """ms per step over K timed steps (after W warmups), then per-kernel
         averages from the same steps run again with events around each
         launch: (ms_per_step, first-kernel ms list, second-kernel ms list)."""
-        t_end = time.perf_counter() + args.settle_ms * 1e-3
-        while time.perf_counter() < t_end:  # clock settle, untimed
-            step()
+        with ClockSampler() as clk:  # the clock and power under this load
+            t_end = time.perf_counter() + args.settle_ms * 1e-3
+            while time.perf_counter() < t_end:  # clock settle, untimed
+                step()
+                torch.cuda.synchronize()
+            for _ in range(args.warmup):
+                step()
             torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        # Timed region: K steps between two events, no per-kernel events inside.
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(args.steps):
-            step()
-        end.record(stream)
-        torch.cuda.synchronize()
+            # Timed region: K steps between two events, no per-kernel events inside.
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            for _ in range(args.steps):
+                step()
+            end.record(stream)
+            torch.cuda.synchronize()
+        clocks[step.__name__] = clk.summary()
         ms = start.elapsed_time(end) / args.steps
         ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_layers)]
               for _ in range(args.steps)]
@@ -338,9 +448,9 @@ def main():
         return ms, k1, k2
 
     Sq = layers[0]["Sq"]
-    fl_layer = attn_flops(1, S, Dv=args.dv, Sq=Sq)
-    pb = proj_bytes(P, 128)
-    pf = proj_flops(P, 128)
+    fl_layer = attn_flops(Bw, S, Dv=args.dv, Sq=Sq)
+    pb = proj_bytes(P, 128) * n_pairs
+    pf = proj_flops(P, 128) * n_pairs
     if path == "pair":
         ms_per_step, fused_ms, _ = measure(step_pair)
         kern_ms = fused_ms
@@ -411,8 +521,8 @@ def main():
     rec = {
         "metric": ("biased-MQA fwd TFLOP/s at S=8192, H=8, d=128 bf16; % MFMA peak"
                    if (args.dv == 128 and wl == "full") else
-                   f"biased-MQA fwd TFLOP/s at S={S}, Sq={Sq}, H=8, dk=128, dv={args.dv} bf16; "
-                   f"% MFMA peak"),
+                   f"biased-MQA fwd TFLOP/s at B={Bw}, S={S}, Sq={Sq}, H=8, dk=128, dv={args.dv} "
+                   f"bf16; % MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -430,19 +540,31 @@ def main():
                                 "mid": "mid: independent S=2048 layers, each pair-bias projection "
                                        "+ biased soft-capped MQA fwd",
                                 "shard": "one GPU's share of full-context layers (queries "
-                                         "3072..4095 of 8192, all keys; full projection)"}[wl],
+                                         "3072..4095 of 8192, all keys; full projection)",
+                                "variant": "variant batch: one call on 8 items of S=8192, 4 "
+                                           "ref/alt pairs (alt = ref + noise on rows "
+                                           "4090..4101), one pair representation per pair",
+                                "stress": "stress: one call at S=16384 (P=1024), pair-bias "
+                                          "projection + biased soft-capped MQA fwd"}[wl],
                    "route": {"pair": "pair form: projection inside the attention kernel",
                              "two": "projection kernel + attention kernel"}[path],
-                   "B": 1, "S": S, "Sq": Sq, "kv_splits": layers[0]["z"], "P": P, "q_heads": 8,
+                   "B": Bw, "S": S, "Sq": Sq, "kv_splits": layers[0]["z"], "P": P, "q_heads": 8,
                    "kv_heads": 1, "d": 128, "dv": args.dv,
                    "pair_channels": 128, "layers": n_layers, "softcap": cap,
-                   "global_batch": 1, "seq_len": S, "parallelism": "none (1 GPU)"},
+                   "global_batch": Bw, "seq_len": S, "parallelism": "none (1 GPU)"},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": counters["hbm_bytes_per_launch"] if counters else None,
                      "mfma_flops_counter": counters["mfma_flops_per_launch"] if counters else None,
                      "mfma_busy_frac_counter": counters["mfma_busy_frac"] if counters else None,
+                     # GPU cycles per launch from the counters (GRBM_GUI_ACTIVE per XCD) and
+                     # the clock they imply with this run's launch time: the frac on any box
+                     # is flops * clock / (cycles * peak)
+                     "cycles_per_launch_counter": counters.get("cycles_per_launch")
+                     if counters else None,
+                     "implied_clock_mhz": round(counters["cycles_per_launch"] / (kern_avg * 1e3), 1)
+                     if counters and counters.get("cycles_per_launch") else None,
                      "kernel": "biased_mqa_fwd_bf16_capped_kernel" +
                                (" (pair form)" if path == "pair" else ""),
                      "flops_per_launch": kern_fl,
@@ -467,7 +589,8 @@ def main():
                        "peak_GBs": PEAK_HBM_GBS,
                        "frac": round(pb / (proj_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": cpu,
-        "env": environment(torch, dev),
+        "env": {**environment(torch, dev), "host": host_cpu(),
+                "gpu_clock_power": clocks.get("step_pair" if path == "pair" else "step_two")},
     }
     print(json.dumps(rec), flush=True)
 

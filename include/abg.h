@@ -172,6 +172,38 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
                                  int64_t kv_splits, float scale, float softcap,
                                  abg_dtype dtype, void* stream);
 
+/* Bytes of device scratch that abg_biased_mqa_fwd_ex_noalloc holds per GPU. */
+#define ABG_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+/* abg_biased_mqa_fwd_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, meaning and results as abg_biased_mqa_fwd_ex
+ * without the workspace: with kv_splits > 1 the partial numerators and
+ * denominators go to a scratch array that the library itself holds, one copy
+ * per GPU, from the first call on that GPU until the process ends
+ * (ABG_NOALLOC_SCRATCH_BYTES = 64 MiB each).  The call allocates and frees
+ * nothing.
+ *
+ * Limit: abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits) <=
+ * ABG_NOALLOC_SCRATCH_BYTES; a larger request returns ABG_ERR_SHAPE before
+ * anything is enqueued (at Dv = 128 that is B * Sq <= 4064 query positions
+ * with kv_splits = 4, <= 2032 with 8: a 2048-position sequence in 4 key
+ * ranges, or one GPU's 1024 of 8192 query positions in 8).  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents; each call writes all of the partials it
+ * reads before reading them, so nothing needs clearing, but calls that may
+ * overlap in time on one GPU (different streams, different threads without
+ * ordering) race on the array and must be serialised by the caller, e.g. by
+ * issuing them on one stream.  The first call on a device looks up the
+ * array's device address (hipGetSymbolAddress); a failure there returns
+ * ABG_ERR_DEVICE. */
+abg_status abg_biased_mqa_fwd_ex_noalloc(const void* q, const void* k, const void* v,
+                                         const float* bias, void* out,
+                                         int64_t B, int64_t Sq, int64_t Sk, int64_t q_offset,
+                                         int64_t Hq, int64_t Dk, int64_t Dv,
+                                         int64_t bias_batch_stride, int64_t bias_group,
+                                         int64_t kv_splits, float scale, float softcap,
+                                         abg_dtype dtype, void* stream);
+
 /* abg_biased_mqa_fwd_ex with the bias projected inside the attention kernel
  * from the pair representation, so that the compact bias is never written
  * out (page "Making Full-Context AlphaGenome Fit on an RTX 3090", section

@@ -18,12 +18,15 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     AbgError,
     auto_kv_splits,
+    NOALLOC_SCRATCH_BYTES,
     biased_mqa_fwd,
+    biased_mqa_fwd_ex_noalloc,
     load,
     pair_bias_project,
     pair_biased_mqa_fwd,
     raw_biased_mqa_fwd,
     raw_biased_mqa_fwd_ex,
+    raw_biased_mqa_fwd_ex_noalloc,
     raw_pair_bias_project,
     raw_pair_biased_mqa_fwd,
     workspace_bytes,

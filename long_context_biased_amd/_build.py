@@ -14,7 +14,7 @@ LIB_NAME = "libabg.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["biased_mqa_fwd.hip", "pair_bias_project.hip", "abg_api.cpp"]
+SOURCES = ["biased_mqa_fwd.hip", "pair_bias_project.hip", "scratch.hip", "abg_api.cpp"]
 
 # Packed FP32 VALU instructions are disabled for all device code (the
 # compiler would otherwise form v_pk_* from ordinary float code).

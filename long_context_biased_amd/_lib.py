@@ -25,7 +25,12 @@ STATUS = {0: "ABG_OK", 1: "ABG_ERR_NULL", 2: "ABG_ERR_SHAPE", 3: "ABG_ERR_UNSUPP
 #: Every symbol include/abg.h declares.
 EXPORTS = ("abg_abi_version", "abg_status_string", "abg_last_error",
            "abg_pair_bias_project", "abg_biased_mqa_fwd", "abg_biased_mqa_fwd_ex",
-           "abg_biased_mqa_fwd_workspace_bytes", "abg_pair_biased_mqa_fwd")
+           "abg_biased_mqa_fwd_workspace_bytes", "abg_biased_mqa_fwd_ex_noalloc",
+           "abg_pair_biased_mqa_fwd")
+
+#: Device scratch that abg_biased_mqa_fwd_ex_noalloc holds per GPU
+#: (ABG_NOALLOC_SCRATCH_BYTES in include/abg.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class AbgError(RuntimeError):
@@ -66,6 +71,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           i64, i64, i64, i64, i64, i64, f32, f32, i32, vp]
     lib.abg_biased_mqa_fwd_workspace_bytes.restype = i64
     lib.abg_biased_mqa_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.abg_biased_mqa_fwd_ex_noalloc.restype = i32
+    lib.abg_biased_mqa_fwd_ex_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                  i64, i64, i64, i64, i64, f32, f32, i32, vp]
     lib.abg_pair_biased_mqa_fwd.restype = i32
     lib.abg_pair_biased_mqa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                             i64, i64, i64, i64, i64, i64, i64, f32, f32, i32, vp]
@@ -99,6 +107,14 @@ def raw_biased_mqa_fwd_ex(q, k, v, bias, out, workspace, workspace_bytes, B, Sq,
     return load().abg_biased_mqa_fwd_ex(q, k, v, bias, out, workspace, workspace_bytes, B, Sq,
                                         Sk, q_offset, Hq, Dk, Dv, bias_batch_stride,
                                         bias_group, kv_splits, scale, softcap, dtype, stream)
+
+
+def raw_biased_mqa_fwd_ex_noalloc(q, k, v, bias, out, B, Sq, Sk, q_offset, Hq, Dk, Dv,
+                                  bias_batch_stride, bias_group, kv_splits, scale, softcap, dtype,
+                                  stream=None) -> int:
+    return load().abg_biased_mqa_fwd_ex_noalloc(q, k, v, bias, out, B, Sq, Sk, q_offset, Hq, Dk,
+                                                Dv, bias_batch_stride, bias_group, kv_splits,
+                                                scale, softcap, dtype, stream)
 
 
 def raw_pair_biased_mqa_fwd(q, k, v, pair, weight, out, workspace, workspace_bytes, B, Sq, Sk,
@@ -179,22 +195,10 @@ def pair_bias_project(pair, weight, out=None):
     return out[0] if (squeeze and out.dim() == 4) else out
 
 
-def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
-                   softcap: float = 5.0, bias_group: int = 1, q_offset: int = 0,
-                   kv_splits=1, workspace=None):
-    """Biased, soft-capped multi-query attention forward on the GPU.
-
-    ``q`` [B, Sq, 8, 128] holds positions q_offset .. q_offset + Sq - 1 of a
-    sequence whose ``k`` [B, Sk, 1, 128] and ``v`` [B, Sk, 1, Dv] (bfloat16 or
-    float32; Dv 128, or 192 for bf16 with the cap) cover all Sk positions;
-    Sq == Sk and q_offset == 0 is the plain call.  ``bias`` float32 compact
-    bias [8, P, P] (P = ceil(Sk/16)) shared by all items, or [Bb, 8, P, P]
-    with item b reading block b // bias_group.  ``scale`` defaults to
-    1/sqrt(128); ``softcap`` 0 disables the cap.  ``kv_splits`` > 1 (or
-    "auto") computes key ranges in separate workgroups and merges them; the
-    float32 workspace is ``workspace`` or a new device tensor.  Returns
-    ``out`` [B, Sq, 8, Dv] in the input dtype.
-    """
+def _attn_args(q, k, v, bias, out, scale, bias_group):
+    """Shapes, dtypes and strides of an attention call (checks only); returns
+    (B, Sq, Sk, Hq, Dk, Dv, bias_stride, scale, out), with ``out`` a new
+    tensor if None was given."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (bias, "bias")):
         _dev(t, n)
@@ -229,6 +233,28 @@ def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
     _dev(out, "out")
     if out.dtype != q.dtype or tuple(out.shape) != (B, Sq, Hq, Dv):
         raise ValueError("out must match q's dtype and be [B, Sq, Hq, Dv]")
+    return B, Sq, Sk, Hq, Dk, Dv, bias_stride, scale, out
+
+
+def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
+                   softcap: float = 5.0, bias_group: int = 1, q_offset: int = 0,
+                   kv_splits=1, workspace=None):
+    """Biased, soft-capped multi-query attention forward on the GPU.
+
+    ``q`` [B, Sq, 8, 128] holds positions q_offset .. q_offset + Sq - 1 of a
+    sequence whose ``k`` [B, Sk, 1, 128] and ``v`` [B, Sk, 1, Dv] (bfloat16 or
+    float32; Dv 128, or 192 for bf16 with the cap) cover all Sk positions;
+    Sq == Sk and q_offset == 0 is the plain call.  ``bias`` float32 compact
+    bias [8, P, P] (P = ceil(Sk/16)) shared by all items, or [Bb, 8, P, P]
+    with item b reading block b // bias_group.  ``scale`` defaults to
+    1/sqrt(128); ``softcap`` 0 disables the cap.  ``kv_splits`` > 1 (or
+    "auto") computes key ranges in separate workgroups and merges them; the
+    float32 workspace is ``workspace`` or a new device tensor.  Returns
+    ``out`` [B, Sq, 8, Dv] in the input dtype.
+    """
+    import torch
+    B, Sq, Sk, Hq, Dk, Dv, bias_stride, scale, out = _attn_args(q, k, v, bias, out, scale,
+                                                                bias_group)
     if kv_splits == "auto":
         kv_splits = auto_kv_splits(B, Sq, Sk)
     kv_splits = int(kv_splits)
@@ -248,6 +274,26 @@ def biased_mqa_fwd(q, k, v, bias, out=None, *, scale: Optional[float] = None,
                                  out.data_ptr(), ws_ptr, ws_bytes, B, Sq, Sk, int(q_offset), Hq,
                                  Dk, Dv, bias_stride, bias_group, kv_splits, float(scale),
                                  float(softcap), _dtype_code(q), _stream(q.device)))
+    return out
+
+
+def biased_mqa_fwd_ex_noalloc(q, k, v, bias, out, *, scale: Optional[float] = None,
+                              softcap: float = 5.0, bias_group: int = 1, q_offset: int = 0,
+                              kv_splits: int = 1):
+    """``biased_mqa_fwd`` through abg_biased_mqa_fwd_ex_noalloc: the key
+    ranges' partials go to the library's own per-GPU scratch array, so the
+    call allocates nothing (``out`` must be given).  At most
+    NOALLOC_SCRATCH_BYTES of partials; calls on one GPU must not overlap in
+    time (they share that array)."""
+    if out is None:
+        raise ValueError("out must be given: this call allocates nothing")
+    B, Sq, Sk, Hq, Dk, Dv, bias_stride, scale, out = _attn_args(q, k, v, bias, out, scale,
+                                                                bias_group)
+    _check(raw_biased_mqa_fwd_ex_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         bias.data_ptr(), out.data_ptr(), B, Sq, Sk,
+                                         int(q_offset), Hq, Dk, Dv, bias_stride, bias_group,
+                                         int(kv_splits), float(scale), float(softcap),
+                                         _dtype_code(q), _stream(q.device)))
     return out
 
 

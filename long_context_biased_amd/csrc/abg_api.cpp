@@ -46,12 +46,17 @@ abg_status device_status(hipError_t e, const char* what) {
 // representation and projection weight it is projected from (pair, bf16
 // [., P, P, C], and weight [C, Hq]); bias_batch_stride and bias_group then
 // describe pair.
+// With use_scratch the partials of key ranges go to the library's own
+// scratch array instead of a caller's workspace (workspace is ignored): the
+// request is rejected if it needs more than that array holds, and the
+// array's device address is looked up only after every argument passed.
 abg_status attention(const void* q, const void* k, const void* v, const float* bias,
                      const void* pair, const void* weight, int64_t C, void* out,
                      void* workspace, int64_t workspace_bytes, int64_t B, int64_t Sq,
                      int64_t Sk, int64_t q_offset, int64_t Hq, int64_t Dk, int64_t Dv,
                      int64_t bias_batch_stride, int64_t bias_group, int64_t kv_splits,
-                     float scale, float softcap, abg_dtype dtype, void* stream) {
+                     float scale, float softcap, abg_dtype dtype, void* stream,
+                     bool use_scratch = false) {
   if (dtype != ABG_F32 && dtype != ABG_BF16)
     return fail(ABG_ERR_VALUE, "dtype %d is not ABG_F32 or ABG_BF16", (int)dtype);
   if (!q) return fail(ABG_ERR_NULL, "q is NULL");
@@ -87,10 +92,19 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
     return fail(ABG_ERR_SHAPE, "kv_splits = %lld must divide the %lld key tiles", (long long)kv_splits,
                 (long long)tiles);
   const int64_t ws_need = abg_biased_mqa_fwd_workspace_bytes(B, Sq, Hq, Dv, kv_splits);
-  if (kv_splits > 1 && !workspace) return fail(ABG_ERR_NULL, "workspace is NULL (kv_splits > 1)");
-  if (kv_splits > 1 && workspace_bytes < ws_need)
-    return fail(ABG_ERR_SHAPE, "workspace_bytes = %lld, need %lld", (long long)workspace_bytes,
-                (long long)ws_need);
+  if (use_scratch) {
+    if (kv_splits > 1 && (ws_need < 0 || ws_need > abg::kScratchBytes))
+      return fail(ABG_ERR_SHAPE,
+                  "kv_splits = %lld needs %lld bytes of partials; the no-allocation entry point "
+                  "holds at most %lld (use fewer key ranges or fewer query positions per call, "
+                  "or abg_biased_mqa_fwd_ex with a workspace)",
+                  (long long)kv_splits, (long long)ws_need, (long long)abg::kScratchBytes);
+  } else {
+    if (kv_splits > 1 && !workspace) return fail(ABG_ERR_NULL, "workspace is NULL (kv_splits > 1)");
+    if (kv_splits > 1 && workspace_bytes < ws_need)
+      return fail(ABG_ERR_SHAPE, "workspace_bytes = %lld, need %lld", (long long)workspace_bytes,
+                  (long long)ws_need);
+  }
   // the merge of the partials runs one thread per 4 output values in a
   // one-dimensional grid of 256-thread workgroups
   if (kv_splits > 1 && B * Sq * Hq * (Dv / 4) > (int64_t)INT32_MAX * 256)
@@ -121,7 +135,7 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bsrc) || !aligned16(out))
     return fail(ABG_ERR_ALIGN, "q, k, v, %s and out must be 16-byte aligned", pair ? "pair" : "bias");
   if (pair && !aligned16(weight)) return fail(ABG_ERR_ALIGN, "weight must be 16-byte aligned");
-  if (kv_splits > 1 && !aligned16(workspace))
+  if (kv_splits > 1 && !use_scratch && !aligned16(workspace))
     return fail(ABG_ERR_ALIGN, "workspace must be 16-byte aligned");
   const int64_t E = elem_bytes(dtype);
   const int64_t q_bytes = B * Sq * Hq * Dk * E;
@@ -136,7 +150,7 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
   if (overlaps(out, out_bytes, bsrc, bias_bytes))
     return fail(ABG_ERR_ALIAS, "out overlaps %s", pair ? "pair" : "bias");
   if (pair && overlaps(out, out_bytes, weight, w_bytes)) return fail(ABG_ERR_ALIAS, "out overlaps weight");
-  if (kv_splits > 1) {
+  if (kv_splits > 1 && !use_scratch) {
     const void* ins[6] = {q, k, v, bsrc, out, weight};
     const int64_t sz[6] = {q_bytes, kv_bytes, B * Sk * Dv * E, bias_bytes, out_bytes, w_bytes};
     for (int i = 0; i < (pair ? 6 : 5); ++i)
@@ -144,6 +158,11 @@ abg_status attention(const void* q, const void* k, const void* v, const float* b
         return fail(ABG_ERR_ALIAS, "workspace overlaps an input or the output");
   }
 
+  if (kv_splits > 1 && use_scratch) {
+    // the scratch array's device address (never its host-side name)
+    const abg_status st = device_status(abg::scratch_address(&workspace), "scratch address lookup");
+    if (st != ABG_OK) return st;
+  }
   abg::AttnLaunch a{q, k, v, bias, pair, weight, out, static_cast<float*>(workspace), B, Sq, Sk,
                     q_offset, Dv, bias_batch_stride, bias_group, kv_splits, scale, softcap, dtype};
   hipError_t e = abg::launch_biased_mqa_fwd(a, static_cast<hipStream_t>(stream));
@@ -237,6 +256,20 @@ abg_status abg_biased_mqa_fwd_ex(const void* q, const void* k, const void* v,
   return attention(q, k, v, bias, nullptr, nullptr, 0, out, workspace, workspace_bytes, B, Sq, Sk,
                    q_offset, Hq, Dk, Dv, bias_batch_stride, bias_group, kv_splits, scale, softcap,
                    dtype, stream);
+}
+
+abg_status abg_biased_mqa_fwd_ex_noalloc(const void* q, const void* k, const void* v,
+                                         const float* bias, void* out,
+                                         int64_t B, int64_t Sq, int64_t Sk, int64_t q_offset,
+                                         int64_t Hq, int64_t Dk, int64_t Dv,
+                                         int64_t bias_batch_stride, int64_t bias_group,
+                                         int64_t kv_splits, float scale, float softcap,
+                                         abg_dtype dtype, void* stream) {
+  g_last_error.clear();
+  if (!bias) return fail(ABG_ERR_NULL, "bias is NULL");
+  return attention(q, k, v, bias, nullptr, nullptr, 0, out, nullptr, 0, B, Sq, Sk, q_offset, Hq,
+                   Dk, Dv, bias_batch_stride, bias_group, kv_splits, scale, softcap, dtype, stream,
+                   true);
 }
 
 abg_status abg_pair_biased_mqa_fwd(const void* q, const void* k, const void* v,

@@ -34,6 +34,14 @@ struct AttnLaunch {
 
 hipError_t launch_biased_mqa_fwd(const AttnLaunch& a, hipStream_t stream);
 
+// Bytes of the library-owned scratch array that abg_biased_mqa_fwd_ex_noalloc
+// uses in place of a caller's workspace (one copy per GPU).
+constexpr int64_t kScratchBytes = ABG_NOALLOC_SCRATCH_BYTES;
+
+// Device address of that array on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached).
+hipError_t scratch_address(void** ptr);
+
 hipError_t launch_pair_bias_project(const void* pair, const void* weight, float* bias,
                                     int64_t Bp, int64_t P, int64_t C, abg_dtype dtype,
                                     hipStream_t stream);

@@ -127,6 +127,53 @@ def test_attention_ex_rejects(kw, code):
     assert abg.load().abg_last_error().decode()
 
 
+def attn_noalloc(**kw):
+    a = dict(q=Q, k=K, v=V, bias=BIAS, out=OUT, B=1, Sq=1024, Sk=8192, q_offset=3072, Hq=8,
+             Dk=128, Dv=128, bias_batch_stride=0, bias_group=1, kv_splits=8, scale=0.088,
+             softcap=5.0, dtype=BF16)
+    a.update(kw)
+    return abg.raw_biased_mqa_fwd_ex_noalloc(a["q"], a["k"], a["v"], a["bias"], a["out"], a["B"],
+                                             a["Sq"], a["Sk"], a["q_offset"], a["Hq"], a["Dk"],
+                                             a["Dv"], a["bias_batch_stride"], a["bias_group"],
+                                             a["kv_splits"], a["scale"], a["softcap"], a["dtype"],
+                                             None)
+
+
+# The no-allocation entry point validates everything before its scratch
+# lookup (the only HIP call before the launch), so these run without a GPU.
+# Every case must stay invalid: the pointers are not device memory.
+NOALLOC_CASES = [
+    (dict(q=None), NULL), (dict(bias=None), NULL), (dict(out=None), NULL),
+    (dict(out=Q), ALIAS), (dict(Hq=4), UNSUP), (dict(kv_splits=3), SHAPE),
+    (dict(kv_splits=0), SHAPE), (dict(q_offset=8), UNSUP), (dict(scale=float("nan")), VALUE),
+    # partials past the 64 MiB scratch: 8 ranges x 8192 rows x 8 heads x 129 x 4 B
+    (dict(Sq=8192, q_offset=0), SHAPE),
+    # just past: 2033 positions x 8 ranges need 67,141,888 B > 67,108,864 B
+    (dict(Sq=2048 + 1, q_offset=0), SHAPE), (dict(B=2, Sq=1024 + 16, Sk=8192), SHAPE),
+    (dict(Dv=192, Sq=1400, q_offset=0), SHAPE), (dict(softcap=0.0, Sq=4096, q_offset=0), SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,code", NOALLOC_CASES, ids=lambda x: str(x))
+def test_noalloc_rejects(kw, code):
+    st = attn_noalloc(**kw)
+    assert st == code, (st, abg.load().abg_last_error())
+    msg = abg.load().abg_last_error().decode()
+    assert msg
+    if code == SHAPE and "Sq" in kw and kw.get("q_offset") == 0 and kw.get("Sq", 0) > 2048:
+        assert "no-allocation" in msg, msg
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ABG_NOALLOC_SCRATCH_BYTES \((\d+)LL << (\d+)\)", text)
+    assert m, "ABG_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the largest request that fits: 8 ranges of 2032 query positions
+    assert abg.workspace_bytes(1, 2032, 8, 128, 8) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert abg.workspace_bytes(1, 2033, 8, 128, 8) > _lib.NOALLOC_SCRATCH_BYTES
+
+
 def pattn(**kw):
     a = dict(q=Q, k=K, v=V, pair=BIAS, weight=WS, out=OUT, ws=None, ws_bytes=0, B=1, Sq=8192,
              Sk=8192, q_offset=0, Hq=8, Dk=128, Dv=128, C=128, pair_batch_stride=0, pair_group=1,
@@ -269,4 +316,5 @@ def test_build_flags():
     assert "--offload-arch=gfx950" in f
     i = f.index("-packed-fp32-ops")
     assert f[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
-    assert set(_build.SOURCES) == {"biased_mqa_fwd.hip", "pair_bias_project.hip", "abg_api.cpp"}
+    assert set(_build.SOURCES) == {"biased_mqa_fwd.hip", "pair_bias_project.hip", "scratch.hip",
+                                   "abg_api.cpp"}

@@ -789,6 +789,23 @@ __device__ __forceinline__ void sm_op_u(int pass, int x, SmState& st, const f32x
   }
 }
 
+// The values of lanes l and l ^ 32 of x, in every lane l (in either order).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; given two copies of x they come out as
+// (x[0..31], x[0..31]) and (x[32..63], x[32..63]).  Written out here: through
+// the compiler's builtin, this toolchain hands back the first result in place
+// of the second (both results came out equal on gfx950), which would drop
+// the other half's value.  The nops keep the instruction's distance from the
+// VALU writes of its operands.
+__device__ __forceinline__ f32x2 swap_halves(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+#pragma clang diagnostic pop
+  return f32x2{__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)};
+}
+
 // Running maximum without the cap (the page's online update, base 2): the
 // maximum of a row over the 32 keys of a half (16 exponents in this lane,
 // 16 in lane l ^ 32).  The reference moves only when some row of the wave
@@ -801,9 +818,8 @@ __device__ __forceinline__ bool update_ref(const f32x16& s, float& mref, float& 
   const float a2 = fmaxf(fmaxf(s[6], s[7]), s[8]), a3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
   const float a4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
   const float m = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[15]));
-  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, m),
-                                                   __builtin_bit_cast(unsigned, m), false, false);
-  const float mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+  const f32x2 sw = swap_halves(m);
+  const float mh = fmaxf(sw.x, sw.y);
   const bool any = __builtin_amdgcn_ballot_w64(mh > mref + 8.f) != 0;
   const float mn = any ? fmaxf(mref, mh) : mref;
   f = __builtin_amdgcn_exp2f(mref - mn);

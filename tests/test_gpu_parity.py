@@ -452,6 +452,34 @@ def test_uncapped_padding_keys_do_not_move_the_maximum(case):
     assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
+# bf16 without the cap: the row maximum of a half combines the two lanes
+# that hold a query row's keys (lane l: keys 0..7 of each 16-key group, lane
+# l ^ 32: keys 8..15).  A key at an odd 8-key position whose logit exceeds
+# every other by about 180 (q = 4 everywhere, that key 4 everywhere) must move
+# the reference maximum; were only one lane's values seen, its weight
+# 2^(u - reference) would overflow float32 (page "Making Full-Context
+# AlphaGenome Fit on an RTX 3090", section "Online softmax, one block at a
+# time": the maximum runs over every key of the block).
+@pytest.mark.parametrize("key,z", [(8, 1), (72, 1), (255, 1), (200, 2)], ids=lambda c: str(c))
+def test_uncapped_maximum_sees_both_lane_halves(key, z):
+    S = 256
+    L = workloads.make_custom(B=1, S=S, dtype="bf16", C=16, seed=2300 + key, qkv_std=1.0 / math.sqrt(128.0),
+                              bias_std=2.0)
+    L.cap = 0.0
+    q = np.full(L.q.shape, 4.0, np.float32)
+    k = np.asarray(oracle.as_f64(L.k), np.float32).copy()
+    k[:, key] = 4.0
+    L.q = workloads.f32_to_bf16_bits(q)
+    L.k = workloads.f32_to_bf16_bits(k)
+    out = _run_ex(L, range(0, S), kv_splits=z)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    ref = oracle.attention_rows(L.q, L.k, L.v, _oracle_bias(L), np.arange(S), scale=L.scale,
+                                cap=0.0, batch=0)
+    ok, ma, rel = attention_ok(out[0], ref, "bf16")
+    print(f"  dominant key {key} z={z}: max-abs {ma:.3g} rel-L2 {rel:.3g}", flush=True)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_attention_long_sampled():
     """S = 65536 (4096 compact cells per side, 1024 key tiles, a 512 MiB
     bias), far past the workloads' lengths: sampled rows, through the

@@ -397,9 +397,12 @@ __device__ __forceinline__ void softmax_half(const f32x16& s, f32x2 beta, float 
 // Fixed-order stage for bf16 with the cap.
 //
 // Softmax micro-operations of one 32-key half (16 values per lane).  The
-// scores arrive as exponents t = alpha s + beta (Q pre-scaled by alpha, the
-// accumulator started from beta):
-//   pass 1: y = exp2(t)   2: d = fma(y, a, a)   3: r = rcp(d)   4: w = exp2(r)
+// scores arrive as exponents t (Q pre-scaled by alpha), and A is the fma's
+// multiplier: with the compact bias t = alpha s (the accumulator started from
+// zero) and the bias cell enters as A = a 2^beta (cap_multiplier); in the
+// pair form t = alpha s + beta (the accumulator started from the expanded
+// offsets) and A = a:
+//   pass 1: y = exp2(t)   2: d = fma(y, A, a)   3: r = rcp(d)   4: w = exp2(r)
 //   pass 5: pack pair k to bf16       6: row sum += the packed pair
 // issued as a skewed pipeline: at step tau, pass p works on value
 // tau - 3 (p - 1), and pair k is packed two steps after its second value is
@@ -441,10 +444,10 @@ struct SmState {
 };
 
 __device__ __forceinline__ void sm_op(int pass, int x, SmState& st, const f32x16& s, float den_a,
-                                      float& rowsum) {
+                                      f32x2 am, float& rowsum) {
   switch (pass) {
     case 1: st.v[x] = __builtin_amdgcn_exp2f(s[x]); break;
-    case 2: st.v[x] = __builtin_fmaf(st.v[x], den_a, den_a); break;
+    case 2: st.v[x] = __builtin_fmaf(st.v[x], x < 8 ? am.x : am.y, den_a); break;
     case 3: st.v[x] = __builtin_amdgcn_rcpf(st.v[x]); break;
     case 4: st.v[x] = __builtin_amdgcn_exp2f(st.v[x]); break;
     case 5: {
@@ -895,6 +898,43 @@ __device__ __forceinline__ f32x16 beta_acc(const char* smem, const int (&xbl)[HP
   return *reinterpret_cast<const f32x16*>(smem + xbl[hh] + S * FP<DV>::XBS + KB * 128);
 }
 
+// The soft-capped weight with the bias cell as a multiplier.  With
+// y = 2^(alpha s) from the MFMA and beta = bias x beta_mul,
+//   exp(L - cap) = exp2(rcp(a (1 + 2^(alpha s + beta)))) = exp2(rcp(fma(y, A, a))),
+//   A = a 2^beta,
+// so the bias needs no work per logit: it scales the fma that the cap needs
+// anyway, and the QK^T accumulator starts from zero.  beta is clamped to
+// [-100, 100]: beyond it the weight is saturated (2^beta's factor moves
+// 1 + 2^(alpha s + beta) by less than 2^-70 relative) unless |alpha s| > 100
+// as well, which needs |scale q.k| above 34.7 cap -- a logit no attention
+// input reaches; inside the range the product is the exact exponent sum up to
+// rounding.
+__device__ __forceinline__ float cap_multiplier(float cell, float beta_mul, float den_a) {
+  return den_a * __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(cell * beta_mul, -100.f, 100.f));
+}
+// The value v holds in lane (l & ~3) + K of each quad.
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xF, 0xF, false));
+}
+// Lane l's compact-bias cell of slot S ([head][query cell][key cell] as
+// copied) for head `head`: query cell (l & 31) >> 4 (its row's), key cell
+// l & 3 of the tile.  AGAIN (the tails): the address is worked out afresh,
+// not kept in a register from the prologue through the whole key loop.
+template <int DV, int S, bool AGAIN = false>
+__device__ __forceinline__ float cell_read(const char* smem, int head) {
+  int lane = (int)threadIdx.x & 63;
+  if constexpr (AGAIN) asm volatile("" : "+v"(lane));
+  const int v = ((lane & 31) >> 4) * 4 + (lane & 3);
+  return reinterpret_cast<const float*>(smem + FP<DV>::B0 + S * 256)[head * 8 + v];
+}
+// The two multipliers of half KB (key cells 2 KB and 2 KB + 1) from the
+// lane values of a tile.
+template <int KB>
+__device__ __forceinline__ f32x2 half_multipliers(float am) {
+  return f32x2{quad_bcast<2 * KB>(am), quad_bcast<2 * KB + 1>(am)};
+}
+
 // x plus the value x holds in the lane that the DPP control CTRL names
 // (within each row of 16 lanes).
 template <int CTRL>
@@ -967,14 +1007,14 @@ __device__ __forceinline__ void valu_group_n(int n) {
 // LDS feeds the MFMAs of all HPW heads.  ring[] holds A fragments three
 // slots ahead; the last three slots fetch the first three fragments of the
 // following stage (PV on half NKB of V stage NSV).
-template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB, bool CAP, bool PROJ = false>
+template <int HPW, int DV, int SV, int SK, int KB, int NSV, int NKB, bool CAP, bool MUL, bool PROJ = false>
 __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
                                        const int (&vro)[DV / 32], const int (&xbl)[HPW],
                                        const bf16x8 (&qf)[HPW][8], f32x16 (&O)[HPW][DV / 32],
                                        f32x16 (&sout)[HPW], const bf16x8 (&pin)[HPW][2],
                                        const f32x16 (&ssm)[HPW], float den_a, float (&rowsum)[HPW],
                                        float (&mref)[HPW], bf16x8 (&pout)[HPW][2], bf16x8 (&ring)[4],
-                                       const ProjIn<HPW>* proj = nullptr) {
+                                       const f32x2 (&amx)[HPW], const ProjIn<HPW>* proj = nullptr) {
   constexpr int NPV = DV / 32;
   constexpr int NSLOT = 8 + 2 * NPV;
   constexpr int NOPS = CAP ? kSmOps : kSmOpsU;
@@ -994,9 +1034,11 @@ __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
   ProjState pst[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) pst[hh] = ProjState{0.f, 0.f, 0.f};
-  f32x16 acc[HPW];  // QK^T of the next half starts from its exponent offsets
+  // QK^T of the next half: from zero when the bias is the softmax's
+  // multiplier (MUL), from its exponent offsets otherwise
+  f32x16 acc[HPW];
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) acc[hh] = beta_acc<HPW, SK, KB, DV>(smem, xbl, hh);
+  for (int hh = 0; hh < HPW; ++hh) acc[hh] = MUL ? f32x16{} : beta_acc<HPW, SK, KB, DV>(smem, xbl, hh);
 #pragma unroll
   for (int j = 0; j < NSLOT; ++j) {
     const int jn = j + 3;
@@ -1017,7 +1059,7 @@ __device__ __forceinline__ void fstage(const char* smem, const int (&kro)[8],
       for (int u = 0; u < sm_count<NSLOT, NOPS>(j); ++u) {
         if constexpr (CAP)
           sm_op(kSm.op[sm_begin<NSLOT>(j) + u].pass, kSm.op[sm_begin<NSLOT>(j) + u].idx, sm[hh],
-                ssm[hh], den_a, rowsum[hh]);
+                ssm[hh], den_a, amx[hh], rowsum[hh]);
         else
           sm_op_u(kSmU.op[sm_begin<NSLOT, NOPS>(j) + u].pass, kSmU.op[sm_begin<NSLOT, NOPS>(j) + u].idx,
                   sm[hh], ssm[hh], mref[hh], rowsum[hh]);
@@ -1244,26 +1286,52 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUS
                                           f32x16 (&S1)[HPW], bf16x8 (&P0)[HPW][2],
                                           bf16x8 (&P1)[HPW][2],
                                           float den_a, float (&rowsum)[HPW], float (&mref)[HPW],
-                                          bf16x8 (&ring)[4]) {
+                                          bf16x8 (&ring)[4], float (&amA)[HPW], float (&amB)[HPW]) {
   constexpr int NXT = (C + 1) % 3, NN = (C + 2) % 3;
+  constexpr bool MUL = CAP && !FUSED;  // the bias cell as the softmax's multiplier
   // K and V of tile t+2 into the stage that held tile t-1, and the cells of
-  // tile t+3 into the slot that held tile t's (expanded two iterations ago);
+  // tile t+3 into the slot that held tile t's (read two iterations ago);
   // past the end the copies are clamped and land where nobody reads again
   issue_kv<HPW, DV, TAIL, FUSED, NN>(smem, c, min(t + 2, last));
   issue_cells<HPW, DV, TAIL, FUSED, C>(smem, c, min(t + 3, last));
   // pair vectors of tile t+2: read during X (value width 128), or after it
   // (192, whose stage leaves no registers for them); its compact-bias cells
-  // are read during X as well
+  // are read during X as well (value width 128)
   bf16x8 pv[2];
-  float bc[HPW];
+  float bc[HPW], amC[HPW];
   if constexpr (FUSED && DV == 128) pair_load<DV, NN>(smem, pv);
-  if constexpr (!FUSED) bias_cells_load<HPW, DV, NN>(smem, c.wave, bc);
+  if constexpr (!FUSED && !CAP) bias_cells_load<HPW, DV, NN>(smem, c.wave, bc);
+  if constexpr (MUL && DV == 128) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) bc[hh] = cell_read<DV, NN>(smem, c.wave * HPW + hh);
+  }
+  // the multipliers of the halves each stage weighs: tile t's second half
+  // (X), tile t+1's first (Y); a alone in the pair form
+  f32x2 amx[HPW], amy[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    amx[hh] = MUL ? half_multipliers<1>(amA[hh]) : f32x2{den_a, den_a};
+    amy[hh] = MUL ? half_multipliers<0>(amB[hh]) : f32x2{den_a, den_a};
+  }
   // X: PV(t, half 0) + QK(t+1, half 0) || softmax(t, half 1) -> P1
-  fstage<HPW, DV, C, NXT, 0, C, 1, CAP>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, mref, P1, ring);
-  if constexpr (FUSED && DV != 128) pair_load<DV, NN>(smem, pv);
-  // the exponent offsets of tile t+2, read by the next iteration
-  if constexpr (FUSED && DV != 128) pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
-  if constexpr (!FUSED) expand_bias_store<HPW, DV, NN>(smem, c.wave, c.beta_mul, bc);
+  fstage<HPW, DV, C, NXT, 0, C, 1, CAP, MUL>(smem, kro, vro, xbl, qf, O, S0, P0, S1, den_a, rowsum, mref, P1, ring,
+                                             amx);
+  // tile t+2: its cell multiplier (compact bias with the cap) or expanded
+  // exponent offsets (otherwise), worked out within this iteration so that
+  // no LDS count is carried across the loop's back edge
+  if constexpr (MUL && DV == 128) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) amC[hh] = cap_multiplier(bc[hh], c.beta_mul, den_a);
+  }
+  if constexpr (MUL && DV != 128) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) bc[hh] = cell_read<DV, NN>(smem, c.wave * HPW + hh);
+  }
+  if constexpr (FUSED && DV != 128) {
+    pair_load<DV, NN>(smem, pv);
+    pair_store<HPW, DV, NN>(smem, pv, c.wreg, c.wave, c.beta_mul);
+  }
+  if constexpr (!FUSED && !CAP) expand_bias_store<HPW, DV, NN>(smem, c.wave, c.beta_mul, bc);
   // Y: PV(t, half 1) + QK(t+1, half 1) || softmax(t+1, half 0) -> P0
   if constexpr (FUSED && DV == 128) {
     // value width 128: the projection of tile t+2 woven into stage Y
@@ -1276,25 +1344,39 @@ __device__ __forceinline__ void fast_iter(char* smem, const FastCtx<HPW, DV, FUS
     for (int hh = 0; hh < HPW; ++hh)
       pj.dst[hh] = reinterpret_cast<float*>(smem + FP<DV>::XB0 + NN * FP<DV>::XBS) +
                    (c.wave * HPW + hh) * 64 + entry;
-    fstage<HPW, DV, C, NXT, 1, NXT, 0, CAP, true>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, mref, P0,
-                                                  ring, &pj);
+    fstage<HPW, DV, C, NXT, 1, NXT, 0, CAP, MUL, true>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, mref,
+                                                       P0, ring, amy, &pj);
   } else {
-    fstage<HPW, DV, C, NXT, 1, NXT, 0, CAP>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, mref, P0, ring);
+    fstage<HPW, DV, C, NXT, 1, NXT, 0, CAP, MUL>(smem, kro, vro, xbl, qf, O, S1, P1, S0, den_a, rowsum, mref, P0,
+                                                 ring, amy);
+  }
+  if constexpr (MUL && DV != 128) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) amC[hh] = cap_multiplier(bc[hh], c.beta_mul, den_a);
   }
   tile_barrier();
+  if constexpr (MUL) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      amA[hh] = amB[hh];
+      amB[hh] = amC[hh];
+    }
+  }
 }
 
-// Soft-capped weights exp(L - cap) of 16 exponents t (t = alpha s + beta
-// from the accumulator), packed as the PV operand; the row sum adds the
-// packed values.  MASK: keys past the end of the sequence get p = 0.
+// Soft-capped weights exp(L - cap) of 16 exponents t from the accumulator,
+// with the half's two fma multipliers am (the cells' cap_multiplier when t =
+// alpha s, den_a when t already holds the offset), packed as the PV operand;
+// the row sum adds the packed values.  MASK: keys past the end of the
+// sequence get p = 0.
 template <bool MASK>
-__device__ __forceinline__ void softmax_exp(const f32x16& t, float den_a, float& rowsum, bf16x8 (&p)[2],
-                                            int lim) {
+__device__ __forceinline__ void softmax_exp(const f32x16& t, float den_a, f32x2 am, float& rowsum,
+                                            bf16x8 (&p)[2], int lim) {
   float w[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     const float y = __builtin_amdgcn_exp2f(t[x]);
-    const float d = __builtin_fmaf(y, den_a, den_a);
+    const float d = __builtin_fmaf(y, x < 8 ? am.x : am.y, den_a);
     w[x] = __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(d));
   }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -1356,18 +1438,26 @@ __device__ __forceinline__ void softmax_exp_u(const f32x16& u_in, float& mref, f
 }
 // The weights of one half, with or without the cap.
 template <bool CAP, bool MASK, int NPV>
-__device__ __forceinline__ void softmax_any(const f32x16& t, float den_a, float& rowsum, float& mref,
+__device__ __forceinline__ void softmax_any(const f32x16& t, float den_a, f32x2 am, float& rowsum, float& mref,
                                             f32x16 (&O)[NPV], bf16x8 (&p)[2], int lim) {
-  if constexpr (CAP) softmax_exp<MASK>(t, den_a, rowsum, p, lim);
+  if constexpr (CAP) softmax_exp<MASK>(t, den_a, am, rowsum, p, lim);
   else softmax_exp_u<MASK, NPV>(t, mref, rowsum, O, p, lim);
 }
 
 // Last tile (stage C): PV of both halves and the softmax of its second half.
-template <int HPW, int DV, bool TAIL, bool CAP, int C>
+template <int HPW, int DV, bool TAIL, bool CAP, int C, bool FUSED>
 __device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, const int (&vro)[DV / 32],
                                           f32x16 (&O)[HPW][DV / 32], const f32x16 (&S1)[HPW],
                                           const bf16x8 (&P0)[HPW][2], float den_a,
-                                          float (&rowsum)[HPW], float (&mref)[HPW]) {
+                                          float (&rowsum)[HPW], float (&mref)[HPW], int head0, float beta_mul) {
+  // the tile's cell multipliers (compact bias with the cap), read again from
+  // its slot (which still holds them) rather than carried out of the loop in
+  // registers
+  constexpr bool MUL = CAP && !FUSED;
+  float am[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    am[hh] = MUL ? cap_multiplier(cell_read<DV, C, true>(smem, head0 + hh), beta_mul, den_a) : den_a;
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -1375,12 +1465,18 @@ __device__ __forceinline__ void fast_tail(int klim_half1, const char* smem, cons
       const bf16x8 a = vfrag<DV, C>(smem, vro, db, half);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) mfma(O[hh][db], a, P0[hh][half]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  // the compiler would otherwise hoist the second half's value reads and
+  // products above the softmax and run out of registers at value width 192
+  __builtin_amdgcn_sched_barrier(0);
   bf16x8 P1[HPW][2];
   const int lim = klim_half1 - 8 * lane_g();
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
-    softmax_any<CAP, TAIL, DV / 32>(S1[hh], den_a, rowsum[hh], mref[hh], O[hh], P1[hh], lim);
+    softmax_any<CAP, TAIL, DV / 32>(S1[hh], den_a, MUL ? half_multipliers<1>(am[hh]) : f32x2{den_a, den_a},
+                                    rowsum[hh], mref[hh], O[hh], P1[hh], lim);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -1420,11 +1516,11 @@ __device__ __forceinline__ void k_read_offsets(int r, int g, int (&kro)[8]) {
 // offsets are loaded again here rather than kept from the start: holding
 // them past the pipelined loop costs more registers than that loop leaves.
 // The tile's exponent offsets were expanded two iterations before.
-template <int HPW, int DV, bool CAP, int C>
+template <int HPW, int DV, bool CAP, int C, bool FUSED>
 __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpos0, int Sq, const char* smem,
                                              const int (&vro)[DV / 32], const int (&xbl)[HPW],
                                              f32x16 (&O)[HPW][DV / 32], float alpha, float den_a,
-                                             float (&rowsum)[HPW], float (&mref)[HPW]) {
+                                             float (&rowsum)[HPW], float (&mref)[HPW], int head0, float beta_mul) {
   // opaque to the compiler, so that it reloads instead of reusing the values
   // read before the loop
   int lane = (int)threadIdx.x & 63;
@@ -1436,13 +1532,18 @@ __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpo
   int kro[8];
   k_read_offsets<DV>(lane & 31, g, kro);
   const int lim = lim0 - 8 * g;
+  constexpr bool MUL = CAP && !FUSED;
+  float am[HPW];  // the tile's cell multipliers (compact bias with the cap), from its slot
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    am[hh] = MUL ? cap_multiplier(cell_read<DV, C, true>(smem, head0 + hh), beta_mul, den_a) : den_a;
   // QK of both halves first, so that Q and the K offsets are dead before
   // the value fragments are read
   f32x16 sc[2][HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    sc[0][hh] = beta_acc<HPW, C, 0, DV>(smem, xbl, hh);
-    sc[1][hh] = beta_acc<HPW, C, 1, DV>(smem, xbl, hh);
+    sc[0][hh] = MUL ? f32x16{} : beta_acc<HPW, C, 0, DV>(smem, xbl, hh);
+    sc[1][hh] = MUL ? f32x16{} : beta_acc<HPW, C, 1, DV>(smem, xbl, hh);
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -1457,7 +1558,10 @@ __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpo
     bf16x8 P[HPW][2];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
-      softmax_any<CAP, true, DV / 32>(sc[kb][hh], den_a, rowsum[hh], mref[hh], O[hh], P[hh], lim - 32 * kb);
+      softmax_any<CAP, true, DV / 32>(sc[kb][hh], den_a,
+                                      MUL ? (kb == 0 ? half_multipliers<0>(am[hh]) : half_multipliers<1>(am[hh]))
+                                          : f32x2{den_a, den_a},
+                                      rowsum[hh], mref[hh], O[hh], P[hh], lim - 32 * kb);
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -1591,30 +1695,41 @@ __device__ __forceinline__ void fast_attention(const __bf16* __restrict__ q, con
   issue_cells<HPW, DV, TAIL, FUSED, 1>(smem, c, min(1, last));
   issue_cells<HPW, DV, TAIL, FUSED, 2>(smem, c, min(2, last));
   tile_barrier();
-  // exponent offsets of tiles 0 and 1 (iteration t expands tile t+2)
+  // tiles 0 and 1: with the cap and the compact bias the cell multipliers of
+  // each lane (iteration t reads tile t+2's), otherwise the expanded exponent
+  // offsets (iteration t expands or projects tile t+2's)
+  constexpr bool MUL = CAP && !FUSED;
+  float amA[HPW], amB[HPW];  // multipliers of tiles t and t+1 (MUL)
   if constexpr (FUSED) {
     bf16x8 pv[2];
     pair_load<DV, 0>(smem, pv);
     pair_store<HPW, DV, 0>(smem, pv, c.wreg, c.wave, beta_mul);
     pair_load<DV, 1>(smem, pv);
     pair_store<HPW, DV, 1>(smem, pv, c.wreg, c.wave, beta_mul);
-  } else {
+  } else if constexpr (!CAP) {
     expand_bias<HPW, DV, 0>(smem, c.wave, beta_mul);
     expand_bias<HPW, DV, 1>(smem, c.wave, beta_mul);
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      amA[hh] = cap_multiplier(cell_read<DV, 0>(smem, c.wave * HPW + hh), beta_mul, den_a);
+      amB[hh] = cap_multiplier(cell_read<DV, 1>(smem, c.wave * HPW + hh), beta_mul, den_a);
+    }
   }
 
   f32x16 S0[HPW], S1[HPW];
   bf16x8 P0[HPW][2], P1[HPW][2];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    S0[hh] = beta_acc<HPW, 0, 0, DV>(smem, xbl, hh);
-    S1[hh] = beta_acc<HPW, 0, 1, DV>(smem, xbl, hh);
+    S0[hh] = MUL ? f32x16{} : beta_acc<HPW, 0, 0, DV>(smem, xbl, hh);
+    S1[hh] = MUL ? f32x16{} : beta_acc<HPW, 0, 1, DV>(smem, xbl, hh);
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       mfma(S0[hh], kfrag<DV, 0>(smem, kro, 0, kc), qf[hh][kc]);
       mfma(S1[hh], kfrag<DV, 0>(smem, kro, 1, kc), qf[hh][kc]);
     }
-    softmax_any<CAP, TAIL, NPV>(S0[hh], den_a, rowsum[hh], mref[hh], O[hh], P0[hh], klim - 8 * g);
+    softmax_any<CAP, TAIL, NPV>(S0[hh], den_a, MUL ? half_multipliers<0>(amA[hh]) : f32x2{den_a, den_a},
+                                rowsum[hh], mref[hh], O[hh], P0[hh], klim - 8 * g);
   }
   // iteration 0 copies tile 3's cells into slot 0, which other waves may
   // still be reading for tile 0 above (later slots are two barriers past
@@ -1634,31 +1749,31 @@ __device__ __forceinline__ void fast_attention(const __bf16* __restrict__ q, con
   while (true) {
     if (t >= lastp) break;
     fast_iter<HPW, DV, TAIL, FUSED, CAP, 0>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum,
-                                            mref, ring);
+                                            mref, ring, amA, amB);
     ++t;
     if (t >= lastp) break;
     fast_iter<HPW, DV, TAIL, FUSED, CAP, 1>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum,
-                                            mref, ring);
+                                            mref, ring, amA, amB);
     ++t;
     if (t >= lastp) break;
     fast_iter<HPW, DV, TAIL, FUSED, CAP, 2>(smem, c, t, last, kro, vro, xbl, qf, O, S0, S1, P0, P1, den_a, rowsum,
-                                            mref, ring);
+                                            mref, ring, amA, amB);
     ++t;
   }
   switch (lastp % 3) {
-    case 0: fast_tail<HPW, DV, TAIL, CAP, 0>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref); break;
-    case 1: fast_tail<HPW, DV, TAIL, CAP, 1>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref); break;
-    default: fast_tail<HPW, DV, TAIL, CAP, 2>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref); break;
+    case 0: fast_tail<HPW, DV, TAIL, CAP, 0, FUSED>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref, c.wave * HPW, beta_mul); break;
+    case 1: fast_tail<HPW, DV, TAIL, CAP, 1, FUSED>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref, c.wave * HPW, beta_mul); break;
+    default: fast_tail<HPW, DV, TAIL, CAP, 2, FUSED>(klim - 64 * lastp - 32, smem, vro, O, S1, P0, den_a, rowsum, mref, c.wave * HPW, beta_mul); break;
   }
   if constexpr (TAIL) {
     if (c.tile_end > 0) {  // uniform; the tile was loaded and its offsets expanded before
       switch (last % 3) {
-        case 0: fast_partial<HPW, DV, CAP, 0>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
-                                           mref); break;
-        case 1: fast_partial<HPW, DV, CAP, 1>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
-                                           mref); break;
-        default: fast_partial<HPW, DV, CAP, 2>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
-                                           mref); break;
+        case 0: fast_partial<HPW, DV, CAP, 0, FUSED>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
+                                           mref, c.wave * HPW, beta_mul); break;
+        case 1: fast_partial<HPW, DV, CAP, 1, FUSED>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
+                                           mref, c.wave * HPW, beta_mul); break;
+        default: fast_partial<HPW, DV, CAP, 2, FUSED>(klim - 64 * last, qb, qpos0, Sq, smem, vro, xbl, O, alpha, den_a, rowsum,
+                                           mref, c.wave * HPW, beta_mul); break;
       }
     }
   }

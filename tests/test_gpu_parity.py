@@ -753,14 +753,16 @@ def test_equal_values_and_zero_logits(dt):
                                           ("bias", "bf16", 0.0), ("bias", "f32", 0.0),
                                           ("pair", "bf16", 5.0)])
 def test_saturated_logits(route, dt, cap):
-    """Bias cells far beyond the cap (std 60 against cap 5): the capped
+    """Bias cells far beyond the cap (std 90 against cap 5): the capped
     logits sit at +-cap to within rounding, so exp2 of the tanh argument
     overflows to inf or underflows to 0 in float32, and the weights must
     still come out as exp(0) = 1 and exp(-2 cap); without the cap the
-    running maximum jumps by tens at a time.  300 positions: a partial last
-    tile and query block."""
+    running maximum jumps by tens at a time.  Over a hundred cells lie past
+    34.7 cap, where the bf16 kernel clamps the cell's exponent factor
+    2^(2 log2(e) b / cap) at 2^+-100 (the weight is saturated there).  300
+    positions: a partial last tile and query block."""
     L = workloads.make_custom(B=1, S=300, dtype=dt, C=128 if route == "pair" else 16,
-                              seed=4242, qkv_std=1.0, bias_std=60.0)
+                              seed=4242, qkv_std=1.0, bias_std=90.0)
     L.cap = cap
     t = upload(L)
     if route == "pair":
@@ -773,6 +775,7 @@ def test_saturated_logits(route, dt, cap):
     got = to_host(out)
     bias64 = _oracle_bias(L)
     assert float(np.abs(bias64).max()) > 20 * max(cap, 1.0)
+    assert int((np.abs(bias64) > 34.7 * max(cap, 1.0)).sum()) >= 100
     ref = oracle.attention(L.q, L.k, L.v, bias64, scale=L.scale, cap=cap)
     ok, ma, rel = attention_ok(got, ref, dt)
     assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"

@@ -489,6 +489,25 @@ def main():
     torch.cuda.synchronize()
     proj_avg = p0.elapsed_time(p1) / (args.steps * n_layers)
 
+    # The attainable rate beside it: a plain device-to-device copy that moves
+    # as many bytes per launch (half read, half written), back to back over
+    # as many distinct buffers as there are layers.
+    half = pb // 2
+    csrc = [torch.ones(half, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+    cdst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+    for _ in range(args.warmup):
+        for a, b in zip(csrc, cdst):
+            b.copy_(a)
+    torch.cuda.synchronize()
+    p0.record(stream)
+    for _ in range(args.steps):
+        for a, b in zip(csrc, cdst):
+            b.copy_(a)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    copy_avg = p0.elapsed_time(p1) / (args.steps * n_layers)
+    del csrc, cdst
+
     value = n_layers * fl_layer / (ms_per_step * 1e-3) / 1e12
     achieved = kern_fl / (kern_avg * 1e-3) / 1e12
     counters = load_counters(path) if (args.dv == 128 and wl == "full") else None
@@ -498,7 +517,7 @@ def main():
         f"= {achieved:.1f} TFLOP/s")
     log(f"two kernels: attention avg {attn_avg * 1e3:.1f} us, projection interval "
         f"{proj_interval * 1e3:.1f} us; projection alone {proj_avg * 1e3:.1f} us = "
-        f"{pb / (proj_avg * 1e-3) / 1e9:.0f} GB/s")
+        f"{pb / (proj_avg * 1e-3) / 1e9:.0f} GB/s; a copy of as many bytes {copy_avg * 1e3:.1f} us")
 
     if args.copy_mib > 0:
         n = args.copy_mib << 20
@@ -587,7 +606,10 @@ def main():
                        "bytes_per_launch": pb,
                        "achieved_GBs": round(pb / (proj_avg * 1e-3) / 1e9, 1),
                        "peak_GBs": PEAK_HBM_GBS,
-                       "frac": round(pb / (proj_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                       "frac": round(pb / (proj_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "copy_same_bytes": {"avg_launch_us": round(copy_avg * 1e3, 2),
+                                           "achieved_GBs": round(2 * half / (copy_avg * 1e-3) / 1e9, 1)},
+                       "frac_of_copy": round(copy_avg / proj_avg, 4)},
         "cpu_baseline": cpu,
         "env": {**environment(torch, dev), "host": host_cpu(),
                 "gpu_clock_power": clocks.get("step_pair" if path == "pair" else "step_two")},

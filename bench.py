@@ -192,6 +192,11 @@ class ClockSampler:
                 fn = os.path.join(hw, name)
                 if os.access(fn, os.R_OK):
                     self.files.setdefault(key, fn)
+            # without a clock input in hwmon: the device's shader clock
+            # levels, the current one marked with '*'
+            dpm = os.path.join(os.path.dirname(os.path.dirname(hw)), "pp_dpm_sclk")
+            if "freq" not in self.files and os.access(dpm, os.R_OK):
+                self.files["freq_dpm"] = dpm
             if self.files:
                 break
         if "cap" in self.files:
@@ -210,11 +215,29 @@ class ClockSampler:
         except (OSError, ValueError):
             return None
 
+    def _read_dpm(self):
+        fn = self.files.get("freq_dpm")
+        if fn is None:
+            return None
+        try:
+            with open(fn) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        mhz = line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                        return float(mhz.replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
     def _run(self):
         while not self._stop.is_set():
             fq = self._read("freq")
             if fq is not None:
                 self.freq.append(fq / 1e6)
+            else:
+                mhz = self._read_dpm()
+                if mhz is not None:
+                    self.freq.append(mhz)
             pw = self._read("power") if "power" in self.files else self._read("power_in")
             if pw is not None:
                 self.power.append(pw / 1e6)
@@ -233,7 +256,8 @@ class ClockSampler:
             return round(float(np.median(x)), 1) if x else None
         return {"sclk_mhz_median": med(self.freq), "sclk_samples": len(self.freq),
                 "power_w_median": med(self.power), "power_cap_w": self.cap_w,
-                "source": "sysfs hwmon (amdgpu), sampled during the timed region"
+                "source": ("sysfs hwmon (amdgpu)" + (", clock from pp_dpm_sclk" if "freq_dpm" in self.files
+                                                      else "") + ", sampled during the timed region")
                           if self.files else "not readable on this host"}
 
 

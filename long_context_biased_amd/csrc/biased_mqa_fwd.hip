@@ -34,8 +34,10 @@
 //     cells) are staged with it, pre-multiplied by the exponent-domain
 //     constant, and the index (i>>4, j>>4) is fixed per lane and register.
 //     The bf16 kernel (with or without the cap) copies HBM straight to LDS, keeps V
-//     row-major and reads it transposed, and starts each QK^T accumulator
-//     from the tile's bias offsets (see the block comment of that path);
+//     row-major and reads it transposed, and brings the bias in either as
+//     the soft-cap's fma multiplier (compact bias with the cap) or as the
+//     start of each QK^T accumulator (the pair form, and without the cap;
+//     see the block comment of that path);
 //   * software pipeline: a 64-key tile is two 32-key halves.  Each stage
 //     issues 16 MFMAs (PV of one half + QK^T of the next tile's half) and,
 //     woven between them, the soft-cap/softmax chain of another half, so the
@@ -723,9 +725,12 @@ void biased_mqa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
 // bias is projected in the kernel) at 96.75 KiB + s * 2 KiB, exponent
 // offsets expanded to the accumulator layout at 102.75 KiB + s * 2 KiB.
 // The softmax exponent comes out of the MFMA: Q is scaled by the exponent
-// factor when it is loaded, and each QK^T accumulator starts from the
-// tile's expanded offsets (bias x exponent factor), written one iteration
-// ahead by the wave that reads them.  Tiles arrive straight from HBM with
+// factor when it is loaded.  With the compact bias and the cap each lane
+// reads its own cell of the tile and scales the soft-cap's fma by it
+// (cap_multiplier), the accumulator starting from zero; in the pair form and
+// without the cap each QK^T accumulator starts from the tile's expanded
+// offsets (bias x exponent factor), written one iteration ahead by the wave
+// that reads them.  Tiles arrive straight from HBM with
 // global_load_lds_dwordx4 (16 bytes per lane, no register staging); each lane
 // fetches the chunk that belongs at its LDS slot, which applies the layouts:
 //   * K: LDS row kb*32 + rho holds key kb*32 + key_perm(rho); its 16-byte
@@ -1002,7 +1007,8 @@ __device__ __forceinline__ void valu_group_n(int n) {
 
 // One stage: for each of the HPW heads of the wave, 8 + 2 DV/32 MFMAs (PV of
 // half KB of the tile in V stage SV, QK^T of half KB of the tile in K stage
-// SK, its accumulator started from that half's exponent offsets) woven with
+// SK, its accumulator started from zero when the bias is the softmax's
+// multiplier (MUL), else from that half's exponent offsets) woven with
 // the softmax of the exponents `ssm` into `pout`.  Each A fragment read from
 // LDS feeds the MFMAs of all HPW heads.  ring[] holds A fragments three
 // slots ahead; the last three slots fetch the first three fragments of the
@@ -1515,7 +1521,8 @@ __device__ __forceinline__ void k_read_offsets(int r, int g, int (&kro)[8]) {
 // qpos0 of this workgroup (rows past Sq read row Sq - 1).  Q and the K
 // offsets are loaded again here rather than kept from the start: holding
 // them past the pipelined loop costs more registers than that loop leaves.
-// The tile's exponent offsets were expanded two iterations before.
+// The tile's cells (or its expanded exponent offsets: the pair form, and
+// without the cap) were staged two iterations before.
 template <int HPW, int DV, bool CAP, int C, bool FUSED>
 __device__ __forceinline__ void fast_partial(int lim0, const __bf16* qb, int qpos0, int Sq, const char* smem,
                                              const int (&vro)[DV / 32], const int (&xbl)[HPW],

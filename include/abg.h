@@ -120,6 +120,13 @@ abg_status abg_pair_bias_project(const void* pair, const void* weight, float* bi
  * multiple of 4); scale finite; softcap finite and >= 0.  Any other request returns
  * ABG_ERR_UNSUPPORTED, ABG_ERR_SHAPE or ABG_ERR_VALUE before anything is
  * enqueued.
+ *
+ * Range (ABG_BF16 with softcap > 0): the bias cell scales the soft-cap's
+ * exponential by 2^(2 log2(e) bias / softcap), clamped to 2^+-100, so a
+ * bias beyond +-34.66 softcap counts as +-34.66 softcap: the logit is
+ * saturated there and the result is unchanged, unless the pre-cap score
+ * scale * q.k itself exceeds about 30.8 softcap in magnitude with the
+ * opposite sign.
  */
 abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
                               const float* bias, void* out,

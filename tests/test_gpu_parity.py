@@ -480,6 +480,45 @@ def test_uncapped_maximum_sees_both_lane_halves(key, z):
     assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
+# bf16 with the cap and the compact bias: the cell enters as the fma's
+# multiplier a 2^beta with beta = 2 log2(e) bias / cap clamped to +-100, which
+# leaves the weight exact to rounding while |scale q.k| stays below about
+# 30.8 cap (page "Making Full-Context AlphaGenome Fit on an RTX 3090",
+# section "Why stock FlashAttention was not a drop-in replacement": the bias
+# sits inside the cap, so any bias past the cap saturates the logit).  Here
+# every score is +-119.5 (q = 3.25 everywhere, keys of either sign) against
+# cells of +-300, +-120, +-48 and 0: the +-300 cells lie past the clamp and
+# the scores of either sign pull against them.
+@pytest.mark.parametrize("z", [1, 5])
+def test_multiplier_clamp_region(z):
+    S = 320
+    L = workloads.make_custom(B=1, S=S, dtype="bf16", C=16, seed=7100 + z,
+                              qkv_std=1.0 / math.sqrt(128.0))
+    L.cap = 5.0
+    P = L.pair.shape[1]
+    rng = np.random.Generator(np.random.PCG64(7200 + z))
+    cells = rng.choice(np.array([-300, -120, -48, 0, 48, 120, 300], np.float32), size=(1, P, P, 8))
+    pair = np.zeros((1, P, P, 16), np.float32)
+    pair[..., :8] = cells
+    w = np.zeros((16, 8), np.float32)
+    w[np.arange(8), np.arange(8)] = 1.0
+    L.pair = workloads.f32_to_bf16_bits(pair)
+    L.weight = workloads.f32_to_bf16_bits(w)
+    signs = rng.choice(np.array([-1.0, 1.0], np.float32), size=(1, S, 1, 1))
+    L.q = workloads.f32_to_bf16_bits(np.full(L.q.shape, 3.25, np.float32))
+    L.k = workloads.f32_to_bf16_bits(np.broadcast_to(3.25 * signs, L.k.shape))
+    bias64 = _oracle_bias(L)
+    beta = 2.0 * math.log2(math.e) * np.abs(bias64) / L.cap
+    assert int((beta > 100).sum()) > 100 and float(np.abs(bias64).max()) == 300.0
+    s = L.scale * 128 * 3.25 ** 2
+    assert 100 < s < 30.8 * L.cap
+    out = _run_ex(L, range(0, S), kv_splits=z)
+    ref = oracle.attention(L.q, L.k, L.v, bias64, scale=L.scale, cap=L.cap)
+    ok, ma, rel = attention_ok(out, ref, "bf16")
+    print(f"  clamp region z={z}: max-abs {ma:.3g} rel-L2 {rel:.3g}", flush=True)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_attention_long_sampled():
     """S = 65536 (4096 compact cells per side, 1024 key tiles, a 512 MiB
     bias), far past the workloads' lengths: sampled rows, through the

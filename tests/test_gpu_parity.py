@@ -15,7 +15,8 @@ import torch
 
 import oracle
 from gpu_util import sample_rows, to_gpu, to_host, upload
-from long_context_biased_amd import biased_mqa_fwd, pair_bias_project, pair_biased_mqa_fwd, workloads
+from long_context_biased_amd import (biased_mqa_fwd, biased_mqa_fwd_ex_noalloc, pair_bias_project,
+                                     pair_biased_mqa_fwd, workloads)
 from long_context_biased_amd import workspace_bytes as abg_workspace_bytes
 from parity import attention_ok, attention_ok_long, projection_ok
 
@@ -864,9 +865,11 @@ def test_deterministic_and_stream_ordered():
 def test_graph_capture_replays():
     """The calls capture into a HIP graph (through torch.cuda.graph) and every
     replay equals the eager result bit for bit: the plain call, key ranges
-    with a caller-owned workspace, the pair form, and the generic kernel
-    (float32, no cap) with key ranges.  Eager work runs between the
-    replays, and each replay is checked on its own."""
+    with a caller-owned workspace, the pair form, the generic kernel
+    (float32, no cap) with key ranges, and key ranges through the entry
+    point that allocates nothing (its partials in the library's scratch
+    array).  Eager work runs between the replays, and each replay is
+    checked on its own."""
     L = workloads.make_custom(B=1, S=1000, dtype="bf16", C=128, seed=77, qkv_std=1.0, bias_std=2.0)
     t = upload(L)
     bias = pair_bias_project(t["pair"], t["weight"])
@@ -875,7 +878,8 @@ def test_graph_capture_replays():
     tf = upload(F)
     fbias = pair_bias_project(tf["pair"], tf["weight"])
     ws2 = torch.empty(abg_workspace_bytes(1, 1000, 8, 128, 4), dtype=torch.uint8, device="cuda")
-    outs = [torch.empty_like(t["q"]) for _ in range(3)] + [torch.empty_like(tf["q"])]
+    outs = ([torch.empty_like(t["q"]) for _ in range(3)] + [torch.empty_like(tf["q"])]
+            + [torch.empty_like(t["q"])])
 
     def calls():
         biased_mqa_fwd(t["q"], t["k"], t["v"], bias, outs[0], scale=L.scale, softcap=L.cap)
@@ -885,6 +889,8 @@ def test_graph_capture_replays():
                             scale=L.scale, softcap=L.cap)
         biased_mqa_fwd(tf["q"], tf["k"], tf["v"], fbias, outs[3], scale=F.scale, softcap=0.0,
                        kv_splits=4, workspace=ws2)
+        biased_mqa_fwd_ex_noalloc(t["q"], t["k"], t["v"], bias, outs[4], scale=L.scale,
+                                  softcap=L.cap, kv_splits=4)
 
     calls()
     torch.cuda.synchronize()

@@ -138,10 +138,9 @@ abg_status abg_biased_mqa_fwd(const void* q, const void* k, const void* v,
 /* Workspace bytes that abg_biased_mqa_fwd_ex needs for kv_splits key ranges:
  * 0 for kv_splits == 1, else kv_splits * B * Sq * Hq * (Dv + 1) * 4: room for
  * float32 partial numerators and denominators, which is what the float32
- * kernel stores.  The bf16 kernels store each partial row as Dv float16
- * values scaled by a power of two (11 significant bits relative to the row's
- * largest value) and a float pair (denominator, exponent), so they use
- * Dv * 2 + 8 of each row's (Dv + 1) * 4 bytes.  -1 for out-of-range
+ * kernel stores.  The bf16 kernels store each partial row normalised by its
+ * key range's row sum, in bf16, and one float per row, so they use
+ * Dv * 2 + 4 of each row's (Dv + 1) * 4 bytes.  -1 for out-of-range
  * arguments (any below 1, kv_splits above 64, or a size past INT64_MAX). */
 int64_t abg_biased_mqa_fwd_workspace_bytes(int64_t B, int64_t Sq, int64_t Hq, int64_t Dv,
                                            int64_t kv_splits);

@@ -81,7 +81,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 8;      // query heads (one shared K/V head)
 constexpr int kD = 128;        // head dim of Q/K and of V
@@ -1786,43 +1785,35 @@ __device__ __forceinline__ void fast_attention(const __bf16* __restrict__ q, con
     }
   }
   if constexpr (SPLIT) {
-    // partial rows [split][b][pos][h][DV] as float16, each row scaled by
-    // 2^-e with 2^(e-1) <= its largest magnitude < 2^e (so every value is
-    // below 1 and keeps 11 significant bits relative to that maximum), then
-    // one (d, e) float pair per row [split][b][pos][h]: d the row sum with
-    // the cap; without it the rows are normalised first and d holds
-    // reference + log2(row sum).  Lane (r, g) holds channels
-    // 32 db + 8 j + 4 g .. + 3 of its row (32 x 32 accumulator layout);
-    // lanes r and r + 32 share the row.
+    // partial rows [split][b][pos][h][DV], each normalised by its own row
+    // sum and rounded to bf16 (every value a weighted mean of V rows, so in
+    // range and with bf16's own 8-bit exponent per value), then one float per
+    // row [split][b][pos][h]: the row sum with the cap, reference +
+    // log2(row sum) without it.  Lane (r, g) holds channels
+    // 32 db + 8 j + 4 g .. + 3 of its row (32 x 32 accumulator layout).
     const int64_t rows = (int64_t)gridDim.y * Sq * kHeads;
     const int64_t row0 = ((int64_t)split * gridDim.y + b) * Sq * kHeads;
-    _Float16* wn = reinterpret_cast<_Float16*>(ws) + row0 * DV;
-    f32x2* wd = reinterpret_cast<f32x2*>(reinterpret_cast<_Float16*>(ws) + (int64_t)gridDim.z * rows * DV) + row0;
+    __bf16* wn = reinterpret_cast<__bf16*>(ws) + row0 * DV;
+    float* wd = reinterpret_cast<float*>(reinterpret_cast<__bf16*>(ws) + (int64_t)gridDim.z * rows * DV) + row0;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = w * HPW + hh;
       const float tot = rowsum[hh] + __shfl_xor(rowsum[hh], 32);
-      const float inv = CAP ? 1.f : 1.f / tot;
-      float mx = 0.f;
-#pragma unroll
-      for (int db = 0; db < NPV; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, __builtin_fabsf(O[hh][db][i]));
-      const f32x2 sw = swap_halves(mx);
-      mx = fmaxf(sw.x, sw.y) * inv;
-      const int e = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-      const float sc = __builtin_amdgcn_ldexpf(inv, -e);
+      const float inv = 1.f / tot;
       if (TAIL && qpos0 + r >= Sq) continue;
-      _Float16* nrow = wn + ((int64_t)(qpos0 + r) * kHeads + h) * DV + 4 * g;
+      __bf16* nrow = wn + ((int64_t)(qpos0 + r) * kHeads + h) * DV + 4 * g;
 #pragma unroll
       for (int db = 0; db < NPV; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 x = {O[hh][db][4 * j], O[hh][db][4 * j + 1], O[hh][db][4 * j + 2], O[hh][db][4 * j + 3]};
-          *reinterpret_cast<f16x4*>(nrow + 32 * db + 8 * j) = __builtin_convertvector(x * sc, f16x4);
+          const f32x2 lo = {O[hh][db][4 * j] * inv, O[hh][db][4 * j + 1] * inv};
+          const f32x2 hi = {O[hh][db][4 * j + 2] * inv, O[hh][db][4 * j + 3] * inv};
+          u32x2 pk;
+          pk.x = __builtin_bit_cast(unsigned int, __builtin_convertvector(lo, bf16x2));
+          pk.y = __builtin_bit_cast(unsigned int, __builtin_convertvector(hi, bf16x2));
+          *reinterpret_cast<u32x2*>(nrow + 32 * db + 8 * j) = pk;
         }
-      if (g == 0)
-        wd[(int64_t)(qpos0 + r) * kHeads + h] = f32x2{CAP ? tot : mref[hh] + __builtin_amdgcn_logf(tot), (float)e};
+      if (g == 0) wd[(int64_t)(qpos0 + r) * kHeads + h] = CAP ? tot : mref[hh] + __builtin_amdgcn_logf(tot);
     }
   } else {
     __syncthreads();  // the output staging reuses the tile buffers
@@ -1908,35 +1899,34 @@ void merge_partials_kernel(const float* __restrict__ ws, T* __restrict__ out, in
   }
 }
 
-// The same merge for the bf16 kernels' float16 partials (rows scaled by
-// 2^-e, one (d, e) pair per row): out = sum_z 2^e_z n_z / sum_z d_z with the
-// cap; with M = max_z l_z, out = sum_z 2^(l_z - M + e_z) o_z / sum_z
-// 2^(l_z - M) without it.  bf16 output.
+// The same merge for the bf16 kernels' partials (rows normalised by their
+// range's row sum, in bf16; one float per row): with weights w_z = d_z (the
+// cap) or 2^(l_z - M), M = max_z l_z (without it),
+// out = sum_z w_z o_z / sum_z w_z.  bf16 output.
 template <int DV, bool LSE>
 __global__ __launch_bounds__(256)
-void merge_partials16_kernel(const void* __restrict__ ws, __bf16* __restrict__ out, int64_t rows,
-                             int splits) {
+void merge_partials_bf16_kernel(const void* __restrict__ ws, __bf16* __restrict__ out, int64_t rows,
+                                int splits) {
   constexpr int Q = DV / 4;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= rows * Q) return;
   const int64_t row = id / Q;
   const int c4 = (int)(id - row * Q);
-  const _Float16* wn = static_cast<const _Float16*>(ws);
-  const f32x2* wd = reinterpret_cast<const f32x2*>(wn + (int64_t)splits * rows * DV);
+  const __bf16* wn = static_cast<const __bf16*>(ws);
+  const float* wd = reinterpret_cast<const float*>(wn + (int64_t)splits * rows * DV);
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f, mx = -__builtin_inff();
   if constexpr (LSE) {
-    for (int z = 0; z < splits; ++z) mx = __builtin_fmaxf(mx, wd[(int64_t)z * rows + row].x);
+    for (int z = 0; z < splits; ++z) mx = __builtin_fmaxf(mx, wd[(int64_t)z * rows + row]);
   }
   for (int z = 0; z < splits; ++z) {
-    const f32x2 de = wd[(int64_t)z * rows + row];
-    const f16x4 hv = *reinterpret_cast<const f16x4*>(wn + ((int64_t)z * rows + row) * DV + 4 * c4);
-    const float wz = LSE ? __builtin_amdgcn_exp2f(de.x - mx) : 1.f;
-    const int e = (int)de.y;
-    const f32x4 x = __builtin_convertvector(hv, f32x4) * wz;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) num[i] += __builtin_amdgcn_ldexpf(x[i], e);
-    den += LSE ? wz : de.x;
+    const float d = wd[(int64_t)z * rows + row];
+    const u32x2 pk = *reinterpret_cast<const u32x2*>(wn + ((int64_t)z * rows + row) * DV + 4 * c4);
+    const float wz = LSE ? __builtin_amdgcn_exp2f(d - mx) : d;
+    const f32x4 x = {__builtin_bit_cast(float, pk.x << 16), __builtin_bit_cast(float, pk.x & 0xffff0000u),
+                     __builtin_bit_cast(float, pk.y << 16), __builtin_bit_cast(float, pk.y & 0xffff0000u)};
+    num += wz * x;
+    den += wz;
   }
   const float inv = 1.0f / den;
   const f32x2 a = {num[0] * inv, num[1] * inv};
@@ -1979,7 +1969,7 @@ hipError_t launch_fast_t(const AttnLaunch& a, hipStream_t stream, float alpha, f
   if (e != hipSuccess) return e;
   const int64_t rows = a.B * a.Sq * kHeads;
   const int64_t threads = rows * (DV / 4);
-  hipLaunchKernelGGL((merge_partials16_kernel<DV, !CAP>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((merge_partials_bf16_kernel<DV, !CAP>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      stream, a.ws, out, rows, splits);
   return hipGetLastError();
 }

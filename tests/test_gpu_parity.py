@@ -520,6 +520,30 @@ def test_multiplier_clamp_region(z):
     assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
+# V with a dynamic range of 2^40 within each row: channels 0..63 scaled by
+# 2^20, channels 64..127 by 2^-20.  The output is linear in V (page "Making
+# Full-Context AlphaGenome Fit on an RTX 3090", section "Online softmax, one
+# block at a time": n accumulates p v), so each channel group is held to the
+# bf16 bounds relative to its own scale; the key ranges' partial rows must
+# keep every value's own exponent (a format scaled per row would flush the
+# small half to zero).
+@pytest.mark.parametrize("z,cap", [(1, 5.0), (4, 5.0), (4, 0.0)], ids=lambda c: str(c))
+def test_value_channels_of_very_different_scale(z, cap):
+    S = 512
+    L = workloads.make_custom(B=1, S=S, dtype="bf16", C=16, seed=7300 + z, qkv_std=1.0, bias_std=2.0)
+    L.cap = cap
+    v = np.asarray(oracle.as_f64(L.v), np.float32).copy()
+    v[..., :64] *= 2.0 ** 20
+    v[..., 64:] *= 2.0 ** -20
+    L.v = workloads.f32_to_bf16_bits(v)
+    out = _run_ex(L, range(0, S), kv_splits=z)
+    ref = oracle.attention(L.q, L.k, L.v, _oracle_bias(L), scale=L.scale, cap=cap)
+    for lo, hi, sc in ((0, 64, 2.0 ** 20), (64, 128, 2.0 ** -20)):
+        ok, ma, rel = attention_ok(out[..., lo:hi] / sc, ref[..., lo:hi] / sc, "bf16")
+        print(f"  channels {lo}..{hi - 1} z={z} cap={cap}: max-abs/scale {ma:.3g} rel-L2 {rel:.3g}", flush=True)
+        assert ok, f"channels {lo}..{hi - 1}: max-abs/scale {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_attention_long_sampled():
     """S = 65536 (4096 compact cells per side, 1024 key tiles, a 512 MiB
     bias), far past the workloads' lengths: sampled rows, through the

@@ -739,6 +739,31 @@ def test_pair_form_full_layer_every_output(hot):
     assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
+def test_pair_form_variant_pair_every_output():
+    """The variant batch (8 items, 4 REF/ALT pairs sharing a pair
+    representation each, page "Making Full-Context AlphaGenome Fit on an RTX
+    3090", section "Where I would take it next") through the pair form in one
+    call: every output of the second pair (items 2 and 3) against the dense
+    oracle."""
+    import time
+    L = workloads.make_layer("variant")
+    t = upload(L)
+    out = pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], scale=L.scale,
+                              softcap=L.cap, pair_group=L.bias_group)
+    torch.cuda.synchronize()
+    got = to_host(out)
+    bias64 = _oracle_bias(L)
+    t0 = time.time()
+    rows = np.arange(L.S)
+    for b in (2, 3):
+        ref = oracle.attention_rows(L.q, L.k, L.v, bias64, rows, scale=L.scale, cap=L.cap,
+                                    bias_index=L.bias_index, batch=b)
+        ok, ma, rel = attention_ok(got[b], ref, "bf16")
+        print(f"  variant item {b}, every output: max-abs {ma:.3g} rel-L2 {rel:.3g} "
+              f"(oracle {time.time() - t0:.1f} s)", flush=True)
+        assert ok, f"item {b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 @pytest.mark.parametrize("dt,cap", [("f32", 5.0), ("bf16", 0.0)])
 def test_query_block_generic_kernel(dt, cap):
     """A query block at an offset on the float32 / uncapped kernel."""

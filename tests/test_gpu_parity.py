@@ -739,6 +739,24 @@ def test_pair_form_full_layer_every_output(hot):
     assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
 
 
+def test_pair_form_stress_every_output():
+    """Every output of the S = 16384 layer (1024 compact cells per side)
+    through the pair form, against the dense oracle."""
+    import time
+    L = workloads.make_layer("stress")
+    t = upload(L)
+    out = pair_biased_mqa_fwd(t["q"], t["k"], t["v"], t["pair"], t["weight"], scale=L.scale,
+                              softcap=L.cap)
+    torch.cuda.synchronize()
+    got = to_host(out)
+    t0 = time.time()
+    ref = oracle.attention(L.q, L.k, L.v, _oracle_bias(L), scale=L.scale, cap=L.cap)
+    ok, ma, rel = attention_ok(got, ref, "bf16")
+    print(f"  stress layer, every output: max-abs {ma:.3g} rel-L2 {rel:.3g} "
+          f"(oracle {time.time() - t0:.1f} s)", flush=True)
+    assert ok, f"max-abs {ma:.3g} rel-L2 {rel:.3g}"
+
+
 def test_pair_form_variant_pair_every_output():
     """The variant batch (8 items, 4 REF/ALT pairs sharing a pair
     representation each, page "Making Full-Context AlphaGenome Fit on an RTX
